@@ -1,0 +1,159 @@
+"""Thin ctypes binding over ``libfa.so`` (declared in ``include/fa.h``).
+
+Argument marshalling only: every step of the attention forward runs in the
+library's HIP kernels.  Torch supplies device memory and the current stream.
+If the library is missing, every call raises; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libfa.so"
+
+FA_F32, FA_BF16 = 0, 1
+FA_OK = 0
+ABI_VERSION = 1
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-OK status from the library (message: status name and detail)."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(detail)
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIBNAME)
+
+
+def load_library():
+    """Load libfa.so once and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libfa.so is not built (%s); run __graft_entry__.build() or "
+            "python -m exact_io_aware_fa_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p]
+    lib.fa_fwd.restype = i32
+    lib.fa_decode.argtypes = [i32, p, p, p, p, i32, p, p, i32, i32, i32, i32, f32, p, sz, p]
+    lib.fa_decode.restype = i32
+    lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_status_str.argtypes = [i32]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i32
+    if lib.fa_abi_version() != ABI_VERSION:
+        raise RuntimeError("libfa.so ABI version %d, binding expects %d"
+                           % (lib.fa_abi_version(), ABI_VERSION))
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+def _raise(lib, st: int):
+    name = lib.fa_status_str(st).decode()
+    detail = lib.fa_last_error().decode()
+    raise FaError(st, "%s: %s" % (name, detail) if detail else name)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError("fa supports bfloat16 and float32 tensors, got %s" % t.dtype)
+
+
+def _dev_ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("fa expects device tensors")
+    if not t.is_contiguous():
+        raise ValueError("fa expects contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, scale: float,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """Prefill forward.  q [B,N,Hq,d], k/v [B,Nk,Hkv,d] -> (o [B,N,Hq,d], lse [B,Hq,N] fp32)."""
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D BSHD tensors")
+    B, N, Hq, d = q.shape
+    Bk, Nk, Hkv, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                             tuple(v.shape)))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd(_dtype_code(q), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(out),
+                    _dev_ptr(lse), B, Hq, Hkv, N, Nk, d, 1 if causal else 0, float(scale),
+                    _stream_handle(stream))
+    if st != FA_OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_seqlen_k: int) -> int:
+    return int(load_library().fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           cu_seqlens_k: torch.Tensor, max_seqlen_k: int, scale: float,
+           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None, stream=None):
+    """Varlen decode.  q [B,Hq,d], caches [total,Hkv,d], cu_seqlens_k int32 [B+1] (device)
+    -> (o [B,Hq,d], lse [B,Hq] fp32).  ``workspace`` is a uint8 device tensor of at
+    least ``decode_workspace_bytes`` bytes; one is allocated when omitted."""
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 3 or v_cache.dim() != 3:
+        raise ValueError("q must be [B,Hq,d] and caches [total,Hkv,d]")
+    B, Hq, d = q.shape
+    total, Hkv, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q and caches")
+    if cu_seqlens_k.dtype != torch.int32 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_k must be int32 with B+1 entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = int(lib.fa_decode_workspace_bytes(B, Hq, Hkv, d, int(max_seqlen_k)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.fa_decode(_dtype_code(q), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),
+                       _dev_ptr(cu_seqlens_k), int(max_seqlen_k), _dev_ptr(out), _dev_ptr(lse),
+                       B, Hq, Hkv, d, float(scale), _dev_ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != FA_OK:
+        _raise(lib, st)
+    return out, lse

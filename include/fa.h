@@ -1,0 +1,141 @@
+/*
+ * fa.h -- C ABI of the exact, IO-aware attention forward library (libfa.so)
+ * for AMD MI355X (gfx950).
+ *
+ * The library computes, for every query row i of every (batch b, query head h),
+ *
+ *     O[i] = sum_j softmax_j(scale * q_i . k_j) * v_j     over visible keys j
+ *     LSE[i] = ln sum_j exp(scale * q_i . k_j)             (natural log)
+ *
+ * without ever writing the N x Nk score matrix to device memory: Q, K and V
+ * are tiled along the sequence axis, K/V tiles stream through on-chip memory
+ * and a running row max and row sum rescale the partial output (ai6s.net page,
+ * section "FlashAttention changes the dataflow, not the algorithm").  The
+ * result is exact attention up to floating-point rounding order (same section;
+ * effectstory.com page, section "What is FlashAttention").
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers, owned by the caller, contiguous,
+ *    16-byte aligned, and must stay valid until the enqueued work completes.
+ *    Outputs must not alias inputs.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL means the default
+ *    stream).  Calls return without synchronising; the library never
+ *    allocates device memory, copies between host and device or synchronises.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    error no kernel is launched and no output is touched.  Faults that occur
+ *    while a kernel runs surface at the caller's next synchronisation.
+ *  - Grouped-query attention: Hq must be a multiple of Hkv and query head h
+ *    reads kv head h / (Hq / Hkv) (contiguous groups).
+ *  - head dimension d must be 64 or 128.
+ *  - scale must be finite.
+ *  - The library keeps no mutable global state; calls on different streams
+ *    may run concurrently.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, Hq % Hkv != 0, bad scale, misalignment */
+    FA_ERR_UNSUPPORTED = 2,   /* valid but not implemented: head dim, dtype for this entry point */
+    FA_ERR_WORKSPACE = 3,     /* decode workspace missing or smaller than fa_decode_workspace_bytes */
+    FA_ERR_HIP = 4            /* the HIP runtime rejected a launch */
+} fa_status_t;
+
+typedef enum {
+    FA_F32 = 0,               /* fp32 in, fp32 out, fp32 arithmetic */
+    FA_BF16 = 1               /* bf16 in, bf16 out (round to nearest even), fp32 accumulation */
+} fa_dtype_t;
+
+/*
+ * Prefill / full-sequence forward.
+ *
+ * Computes attention of N query rows against Nk keys for every (b, h)
+ * (ai6s.net page, sections "standard attention's fatal flaw ..." for the
+ * definition and "what ops-transformer adds", second item, for the causal mask
+ * fused into the blockwise softmax).
+ *
+ *   q    [B, N,  Hq,  d]  dtype   (BSHD, row-major, contiguous)
+ *   k, v [B, Nk, Hkv, d]  dtype
+ *   o    [B, N,  Hq,  d]  dtype   output
+ *   lse  [B, Hq, N]       fp32    output, natural-log logsumexp of scale*q.k
+ *                                 over the keys visible to the row
+ *   causal != 0: bottom-right alignment, key j is visible to query i iff
+ *                j <= i + (Nk - N)  (j <= i when N == Nk).  Key tiles that are
+ *                entirely masked are never loaded.
+ *   A row with no visible key (possible only when causal and Nk < N) gets
+ *   O = 0 and LSE = -inf.
+ *   B == 0, N == 0 are no-ops returning FA_OK.  Nk == 0 gives O = 0, LSE = -inf.
+ *
+ * Returns FA_OK or an error status (see above); nothing is enqueued on error.
+ */
+fa_status_t fa_fwd(fa_dtype_t dtype,
+                   const void *q, const void *k, const void *v,
+                   void *o, float *lse,
+                   int B, int Hq, int Hkv, int N, int Nk, int d,
+                   int causal, float scale, void *stream);
+
+/*
+ * Decode forward over a packed, variable-length KV cache (one new query token
+ * per sequence).  Only the real cache length of each sequence is read: no
+ * work is done for keys beyond it (ai6s.net page, section "what
+ * ops-transformer adds", third item).
+ *
+ *   q            [B, Hq, d]       bf16
+ *   k_cache,
+ *   v_cache      [total, Hkv, d]  bf16, sequence b occupies rows
+ *                                 cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *   cu_seqlens_k [B+1]            int32, DEVICE pointer; cu[0] == 0,
+ *                                 non-decreasing.  This cannot be checked
+ *                                 without a synchronisation, so it is a
+ *                                 precondition: every length must be
+ *                                 <= max_seqlen_k and rows must lie inside
+ *                                 the caches.
+ *   max_seqlen_k                  host-side upper bound on every length
+ *   o            [B, Hq, d]       bf16 output
+ *   lse          [B, Hq]          fp32 output (natural log)
+ *   workspace                     device scratch of at least
+ *                                 fa_decode_workspace_bytes(B, Hq, Hkv, d,
+ *                                 max_seqlen_k) bytes, 16-byte aligned, owned
+ *                                 by the caller; its contents on entry do not
+ *                                 matter and on exit are unspecified.  Calls
+ *                                 that share a workspace must be ordered on
+ *                                 one stream.
+ *   Every key of the sequence is visible (for one query at the end of the
+ *   sequence, bottom-right causal alignment shows it all).  A sequence of
+ *   length 0 gets O = 0, LSE = -inf.
+ *   dtype must be FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
+ */
+fa_status_t fa_decode(fa_dtype_t dtype,
+                      const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *cu_seqlens_k, int max_seqlen_k,
+                      void *o, float *lse,
+                      int B, int Hq, int Hkv, int d, float scale,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fa_decode needs for these sizes (0 when no work). */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k);
+
+/* Static, human-readable name of a status code. */
+const char *fa_status_str(fa_status_t status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *fa_last_error(void);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

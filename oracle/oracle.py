@@ -1,0 +1,186 @@
+"""Python side of the fp64 CPU oracle (ctypes over ``oracle/liboracle.so``).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this module.  The GPU path
+(``exact_io_aware_fa_amd``) never imports it, and this module imports nothing
+from that package.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, the textbook definition of
+attention: S = scale*Q K^T, mask, softmax, P V, LSE = m + ln l).  This file only
+marshals arrays: it passes the stored bit patterns of the inputs (f64, f32 or
+bf16) to C, which widens them exactly.
+
+Sources: ai6s.net page, sections "standard attention's fatal flaw is data
+movement, not compute" and "FlashAttention changes the dataflow, not the
+algorithm" (the result equals standard attention); same page, section "what
+ops-transformer adds" (causal mask, variable-length KV cache).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F64, F32, BF16 = 0, 1, 2
+_ERRORS = {1: "invalid argument", 2: "softmax row sum differs from 1 by more than 1e-12",
+           3: "out of memory"}
+
+_default = None
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile an oracle C source into a shared library with gcc (fp64, no fast-math)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+           "-std=c11", "-pthread", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so."""
+    if force or not os.path.exists(_LIB):
+        compile_source(_SRC, _LIB)
+    return _LIB
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    p = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_attn_rows.argtypes = [i32, p, p, p, i32, i32, i32, i32, i32, i32, i32,
+                                     f64, i64, p, p, p, p, p, i32]
+    lib.oracle_attn_rows.restype = i32
+    lib.oracle_decode_rows.argtypes = [i32, p, p, p, p, i32, i32, i32, i32, f64,
+                                       i64, p, p, p, p, i32]
+    lib.oracle_decode_rows.restype = i32
+    lib.oracle_version.restype = i32
+    return lib
+
+
+def _load():
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _default = _bind(_LIB)
+    return _default
+
+
+def load_library(path: str):
+    """Bind another build of an oracle source (used to check that the pins catch
+    deliberately planted mistakes); pass the handle as ``lib=``."""
+    return _bind(path)
+
+
+def _stored(t) -> tuple[np.ndarray, int]:
+    """Contiguous host array holding the stored bits of ``t`` and its dtype code."""
+    if isinstance(t, np.ndarray):
+        t = torch.from_numpy(t)
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float64:
+        return t.numpy(), F64
+    if t.dtype == torch.float32:
+        return t.numpy(), F32
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16), BF16
+    raise TypeError("oracle inputs must be float64, float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise RuntimeError("oracle failed: " + _ERRORS.get(rc, "code %d" % rc))
+
+
+def attention_rows(q, k, v, causal: bool, scale: float, rows, nthreads: int = 0, lib=None):
+    """Prefill attention for selected query rows.
+
+    q [B,N,Hq,d], k/v [B,Nk,Hkv,d] (same dtype); ``rows`` is an int array of
+    shape [R,3] holding (b, h, i).  Returns (o [R,d] float64, lse [R] float64).
+    ``scale`` is used as given (pass the fp32 value the GPU receives).
+    """
+    qa, dt = _stored(q)
+    ka, dk = _stored(k)
+    va, dv = _stored(v)
+    if not (dt == dk == dv):
+        raise TypeError("q, k, v must share a dtype")
+    B, N, Hq, d = qa.shape
+    Bk, Nk, Hkv, dk_ = ka.shape
+    if Bk != B or dk_ != d or va.shape != ka.shape:
+        raise ValueError("shape mismatch between q, k and v")
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    rb = np.ascontiguousarray(rows[:, 0].astype(np.int32))
+    rh = np.ascontiguousarray(rows[:, 1].astype(np.int32))
+    ri = np.ascontiguousarray(rows[:, 2].astype(np.int32))
+    R = rows.shape[0]
+    o = np.zeros((R, d), dtype=np.float64)
+    lse = np.zeros((R,), dtype=np.float64)
+    rc = (lib or _load()).oracle_attn_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), B, Hq, Hkv, N, Nk, d,
+                                  1 if causal else 0, float(scale), R, _ptr(rb), _ptr(rh),
+                                  _ptr(ri), _ptr(o), _ptr(lse), int(nthreads))
+    _check(rc)
+    return o, lse
+
+
+def attention(q, k, v, causal: bool, scale: float, nthreads: int = 0, lib=None):
+    """Full prefill attention.  Returns (o [B,N,Hq,d] float64, lse [B,Hq,N] float64)."""
+    B, N, Hq, d = q.shape
+    bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(N), indexing="ij")
+    rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)   # ordered (b, h, i)
+    o, lse = attention_rows(q, k, v, causal, scale, rows, nthreads, lib)
+    o = o.reshape(B, Hq, N, d).transpose(0, 2, 1, 3).copy()
+    lse = lse.reshape(B, Hq, N)
+    return o, lse
+
+
+def decode_rows(q, k_cache, v_cache, cu_seqlens, scale: float, rows, nthreads: int = 0,
+                lib=None):
+    """Decode attention for selected (b, h) pairs.
+
+    q [B,Hq,d]; k_cache/v_cache [total,Hkv,d]; cu_seqlens int [B+1] (host);
+    ``rows`` int array [R,2] of (b, h).  Returns (o [R,d], lse [R]) in float64.
+    """
+    qa, dt = _stored(q)
+    ka, dk = _stored(k_cache)
+    va, dv = _stored(v_cache)
+    if not (dt == dk == dv):
+        raise TypeError("q and caches must share a dtype")
+    B, Hq, d = qa.shape
+    total, Hkv, dk_ = ka.shape
+    if dk_ != d or va.shape != ka.shape:
+        raise ValueError("shape mismatch between q and caches")
+    cu = np.ascontiguousarray(np.asarray(torch.as_tensor(cu_seqlens).cpu(), dtype=np.int32))
+    if cu.shape != (B + 1,) or (B > 0 and int(cu[-1]) > total):
+        raise ValueError("cu_seqlens must have B+1 entries ending at most at the cache size")
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    rb = np.ascontiguousarray(rows[:, 0].astype(np.int32))
+    rh = np.ascontiguousarray(rows[:, 1].astype(np.int32))
+    R = rows.shape[0]
+    o = np.zeros((R, d), dtype=np.float64)
+    lse = np.zeros((R,), dtype=np.float64)
+    rc = (lib or _load()).oracle_decode_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(cu), B, Hq, Hkv, d,
+                                    float(scale), R, _ptr(rb), _ptr(rh), _ptr(o), _ptr(lse),
+                                    int(nthreads))
+    _check(rc)
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, cu_seqlens, scale: float, nthreads: int = 0, lib=None):
+    """Full decode.  Returns (o [B,Hq,d] float64, lse [B,Hq] float64)."""
+    B, Hq, d = q.shape
+    bb, hh = np.meshgrid(np.arange(B), np.arange(Hq), indexing="ij")
+    rows = np.stack([bb.ravel(), hh.ravel()], axis=1)
+    o, lse = decode_rows(q, k_cache, v_cache, cu_seqlens, scale, rows, nthreads, lib)
+    return o.reshape(B, Hq, d), lse.reshape(B, Hq)

@@ -1,0 +1,35 @@
+"""Scalar brute force of attention on tiny inputs: nested Python lists and the
+``math`` module only, no numpy or torch arithmetic.
+
+It is written independently of the oracle and in a different form: the row's
+logsumexp is taken first, log(fsum(exp(s_j))), with no max subtraction, and each
+weight is exp(s_j - lse).  Inputs must keep |s_j| small enough that exp does not
+overflow.  Visibility is the causal predicate with bottom-right alignment
+(key j visible to query i iff j <= i + Nk - N), as read from the ai6s.net page,
+section "what ops-transformer adds", second item.
+"""
+import math
+
+
+def attention(q, k, v, causal, scale):
+    """q [B][N][Hq][d], k/v [B][Nk][Hkv][d] nested lists -> (o [B][N][Hq][d], lse [B][Hq][N])."""
+    B, N, Hq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Nk, Hkv = len(k[0]), len(k[0][0])
+    group = Hq // Hkv
+    o = [[[[0.0] * d for _ in range(Hq)] for _ in range(N)] for _ in range(B)]
+    lse = [[[0.0] * N for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            for i in range(N):
+                keys = [j for j in range(Nk) if (not causal) or j <= i + Nk - N]
+                if not keys:
+                    lse[b][h][i] = -math.inf
+                    continue
+                s = {j: scale * math.fsum(q[b][i][h][c] * k[b][j][g][c] for c in range(d))
+                     for j in keys}
+                z = math.log(math.fsum(math.exp(s[j]) for j in keys))
+                lse[b][h][i] = z
+                for c in range(d):
+                    o[b][i][h][c] = math.fsum(math.exp(s[j] - z) * v[b][j][g][c] for j in keys)
+    return o, lse

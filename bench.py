@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward hot path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic inputs:
+  * prefill: causal GQA attention, B=1, Hq=64, Hkv=8, N=Nk=8192, d=128, bf16
+    (Llama2-70B-shaped), through fa_fwd;
+  * decode: one query token for each of 32 sequences against a packed bf16 KV
+    cache with lengths drawn uniform on 512..32768 (seed 0), Hq=64, Hkv=8,
+    d=128, through fa_decode.
+Inputs are generated once (seeded) and are resident in HBM before timing.
+
+Prints one JSON line.  `value` is the prefill throughput in TFLOP/s counted as
+4*B*Hq*N*Nk*d/2 (the causal half), measured with HIP events around each
+launch on the launch stream; the decode part is reported beside it in GB/s of
+algorithmic bytes (K and V cache, q, o, lse and cu_seqlens, each once).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --pmc-pass      # one launch of each kernel plus a copy of known
+                                    # size, for rocprofv3 counter collection
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
+METRIC = ("attention fwd TFLOP/s & % bf16 MFMA peak (prefill); "
+          "GB/s & % HBM peak (decode)")
+KERNEL_SOURCES = ["exact_io_aware_fa_amd/csrc/fa_prefill_bf16.hip",
+                  "exact_io_aware_fa_amd/csrc/fa_decode.hip",
+                  "exact_io_aware_fa_amd/csrc/fa_common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PMC_COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
+
+
+def source_digest(path):
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, sources):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources") != {p: source_digest(p) for p in sources}:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def prefill_flops(cfg):
+    f = 4.0 * cfg.B * cfg.Hq * cfg.N * cfg.Nk * cfg.d
+    return f / 2 if cfg.causal else f
+
+
+def decode_bytes(cfg, total_len):
+    kv = 2 * total_len * cfg.Hkv * cfg.d * 2
+    qo = 2 * cfg.B * cfg.Hq * cfg.d * 2
+    return kv + qo + cfg.B * cfg.Hq * 4 + (cfg.B + 1) * 4
+
+
+def cpu_baseline(q, k, v, cfg):
+    """The fp64 oracle on a bounded sample of the prefill workload: every 32nd
+    query row, all heads.  Reported as algorithmic TFLOP/s of the sample."""
+    import numpy as np
+    from oracle import oracle
+    rows = np.array([(0, h, i) for i in range(0, cfg.N, 8) for h in range(cfg.Hq)])
+    visible = (rows[:, 2] + 1 + (cfg.Nk - cfg.N)) if cfg.causal else np.full(len(rows), cfg.Nk)
+    flops = float((4.0 * cfg.d * visible).sum())
+    threads = oracle.DEFAULT_THREADS
+    t0 = time.perf_counter()
+    oracle.attention_rows(q, k, v, cfg.causal, cfg.scale, rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d query rows (every 8th row x %d heads) of the prefill workload, "
+                      "%.1f s wall" % (len(rows), cfg.Hq, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU; this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_io_aware_fa_amd import binding, inputs
+
+    binding.load_library()
+    dev = torch.device("cuda:0")
+    pcfg = inputs.LLAMA70B_GQA_BF16
+    dcfg = inputs.DECODE_VARLEN_BF16
+
+    q, k, v = inputs.prefill_config_inputs(pcfg)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty_like(qd)
+    lse = torch.empty((pcfg.B, pcfg.Hq, pcfg.N), dtype=torch.float32, device=dev)
+
+    dq, kc, vc, cu, lens = inputs.decode_config_inputs(dcfg)
+    max_len = int(lens.max())
+    total_len = int(lens.sum())
+    dqd, kcd, vcd, cud = dq.to(dev), kc.to(dev), vc.to(dev), cu.to(dev)
+    del kc, vc
+    do = torch.empty_like(dqd)
+    dlse = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, binding.decode_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.d, max_len)),
+                     dtype=torch.uint8, device=dev)
+
+    def prefill():
+        binding.fwd(qd, kd, vd, pcfg.causal, pcfg.scale, out=o, lse=lse)
+
+    def decode():
+        binding.decode(dqd, kcd, vcd, cud, max_len, dcfg.scale, out=do, lse=dlse, workspace=ws)
+
+    if args.pmc_pass:
+        src = torch.empty(PMC_COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        prefill()
+        decode()
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_pass": True, "copy_bytes": PMC_COPY_BYTES}))
+        return
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(K):
+        ev[s][0].record()
+        prefill()
+        ev[s][1].record()
+        decode()
+        ev[s][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    pre_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    pre_avg = sum(pre_ms) / K
+    dec_avg = sum(dec_ms) / K
+
+    flops = prefill_flops(pcfg)
+    tflops = flops / (pre_avg * 1e-3) / 1e12
+    dbytes = decode_bytes(dcfg, total_len)
+    gbs = dbytes / (dec_avg * 1e-3) / 1e9
+
+    pre_traffic = measured_traffic("prefill_bf16_kernel", KERNEL_SOURCES[::2])
+    dec_traffic = measured_traffic("decode", KERNEL_SOURCES[1:])
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rounded to bf16)",
+        "config": {
+            "workload": "causal GQA prefill B1 Hq64 Hkv8 N8192 d128 + varlen KV-cache decode "
+                        "32 seqs L512-32768 (sum %d) Hq64 Hkv8 d128" % total_len,
+            "prefill": {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "N": pcfg.N, "Nk": pcfg.Nk,
+                        "d": pcfg.d, "causal": pcfg.causal, "ms": round(pre_avg, 4),
+                        "flops_per_launch": flops},
+            "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d,
+                       "sum_len": total_len, "max_len": max_len, "ms": round(dec_avg, 4),
+                       "bytes_per_launch": dbytes, "GB/s": round(gbs, 1),
+                       "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": pre_traffic},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "traffic": dec_traffic},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(q, k, v, pcfg)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -147,7 +147,9 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    need = int(lib.fa_decode_workspace_bytes(B, Hq, Hkv, d, int(max_seqlen_k)))
+    # no sequence can be longer than the cache holds rows
+    max_seqlen_k = min(int(max_seqlen_k), total)
+    need = int(lib.fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = lib.fa_decode(_dtype_code(q), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),

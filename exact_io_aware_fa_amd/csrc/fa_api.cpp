@@ -1,0 +1,180 @@
+// fa_api.cpp -- the C ABI of libfa.so (declared in include/fa.h): argument
+// validation, split planning for decode, and dispatch to the HIP kernels.
+// Nothing here touches the device before every argument has been checked.
+#include "fa.h"
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_kernels.h"
+
+#define FA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512];
+
+fa_status_t fail(fa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fa_status_t ok() {
+  g_last_error[0] = '\0';
+  return FA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p+bytes) overlaps [r, r+rbytes)?
+bool overlaps(const void* p, size_t bytes, const void* r, size_t rbytes) {
+  if (!p || !r || bytes == 0 || rbytes == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), c = reinterpret_cast<uintptr_t>(r);
+  return a < c + rbytes && c < a + bytes;
+}
+
+// Decode split plan: every sequence's cache is cut into chunks of `chunk`
+// keys (a multiple of the kernel's 256-key granule); the grid aims at about
+// kTargetSplitBlocks workgroups when all caches are as long as the bound.
+constexpr int64_t kTargetSplitBlocks = 2048;
+
+struct SplitPlan {
+  int chunk;
+  int max_splits;
+};
+
+SplitPlan plan_splits(int B, int Hkv, int max_seqlen_k) {
+  const int granule = fa::decode_chunk_granule();
+  SplitPlan p{granule, 0};
+  if (B <= 0 || Hkv <= 0 || max_seqlen_k <= 0) return p;
+  int64_t per_seq = (kTargetSplitBlocks + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
+  if (per_seq < 1) per_seq = 1;
+  int64_t chunk = (max_seqlen_k + per_seq - 1) / per_seq;
+  chunk = (chunk + granule - 1) / granule * granule;
+  if (chunk < granule) chunk = granule;
+  p.chunk = (int)chunk;
+  p.max_splits = (int)((max_seqlen_k + chunk - 1) / chunk);
+  return p;
+}
+
+size_t lse_offset_bytes(int64_t slots, int d) {
+  const size_t o_bytes = (size_t)slots * (size_t)d * sizeof(float);
+  return (o_bytes + 255) / 256 * 256;
+}
+
+}  // namespace
+
+FA_EXPORT int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+FA_EXPORT const char* fa_status_str(fa_status_t status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+FA_EXPORT const char* fa_last_error(void) { return g_last_error; }
+
+FA_EXPORT fa_status_t fa_fwd(fa_dtype_t dtype, const void* q, const void* k, const void* v, void* o,
+                             float* lse, int B, int Hq, int Hkv, int N, int Nk, int d, int causal,
+                             float scale, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || N < 0 || Nk < 0) return fail(FA_ERR_INVALID_ARG, "negative size (B=%d N=%d Nk=%d)", B, N, Nk);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (d <= 0) return fail(FA_ERR_INVALID_ARG, "head dim d=%d", d);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and positive (got %g)", (double)scale);
+  if (B == 0 || N == 0) return ok();
+  // the kernels index rows and work items with 32-bit integers
+  if ((int64_t)B * N > INT32_MAX || (int64_t)B * Nk > INT32_MAX ||
+      (int64_t)B * Hq * ((N + 63) / 64) > INT32_MAX - 8)
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+  // tiles address one (batch, head) slice through 32-bit buffer offsets,
+  // including up to one tile of rows past the end
+  const int64_t es64 = dtype == FA_BF16 ? 2 : 4;
+  if (((int64_t)N + 256) * Hq * d * es64 >= INT32_MAX || ((int64_t)Nk + 256) * Hkv * d * es64 >= INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "one batch of q or k/v exceeds 2 GiB");
+  if (!q || !o || !lse) return fail(FA_ERR_INVALID_ARG, "null q, o or lse pointer");
+  if (Nk > 0 && (!k || !v)) return fail(FA_ERR_INVALID_ARG, "null k or v pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t es = dtype == FA_BF16 ? 2 : 4;
+  const size_t q_bytes = (size_t)B * N * Hq * d * es;
+  const size_t kv_bytes = (size_t)B * Nk * Hkv * d * es;
+  const size_t lse_bytes = (size_t)B * Hq * N * sizeof(float);
+  if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) || overlaps(o, q_bytes, v, kv_bytes) ||
+      overlaps(lse, lse_bytes, q, q_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+      overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, q_bytes))
+    return fail(FA_ERR_INVALID_ARG, "outputs alias inputs or each other");
+
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, N, Nk, d, causal != 0, scale,
+                    reinterpret_cast<hipStream_t>(stream)};
+  const hipError_t e = dtype == FA_BF16 ? fa::launch_prefill_bf16(a) : fa::launch_prefill_f32(a);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+FA_EXPORT size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen_k <= 0) return 0;
+  const SplitPlan p = plan_splits(B, Hkv, max_seqlen_k);
+  const int64_t slots = (int64_t)B * Hq * p.max_splits;
+  return lse_offset_bytes(slots, d) + (size_t)slots * sizeof(float);
+}
+
+FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cu_seqlens_k, int max_seqlen_k, void* o, float* lse, int B,
+                                int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || max_seqlen_k < 0) return fail(FA_ERR_INVALID_ARG, "negative size (B=%d max_seqlen_k=%d)", B, max_seqlen_k);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (d <= 0) return fail(FA_ERR_INVALID_ARG, "head dim d=%d", d);
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and positive (got %g)", (double)scale);
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "decode supports bf16 only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (Hq / Hkv > fa::decode_max_group())
+    return fail(FA_ERR_UNSUPPORTED, "Hq/Hkv=%d above %d", Hq / Hkv, fa::decode_max_group());
+  if (B == 0) return ok();
+  if ((int64_t)B * Hq > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "B*Hq too large");
+  if (!q || !o || !lse || !cu_seqlens_k) return fail(FA_ERR_INVALID_ARG, "null q, o, lse or cu_seqlens_k pointer");
+  if (max_seqlen_k > 0 && (!k_cache || !v_cache)) return fail(FA_ERR_INVALID_ARG, "null cache pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace))
+    return fail(FA_ERR_INVALID_ARG, "tensor and workspace pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "cu_seqlens_k must be 4-byte aligned");
+  const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
+  const size_t qo_bytes = (size_t)B * Hq * d * 2;
+  const size_t lse_bytes = (size_t)B * Hq * sizeof(float);
+  if (overlaps(o, qo_bytes, q, qo_bytes) || overlaps(lse, lse_bytes, q, qo_bytes) ||
+      overlaps(lse, lse_bytes, o, qo_bytes) || overlaps(workspace, need, o, qo_bytes) ||
+      overlaps(workspace, need, lse, lse_bytes) || overlaps(workspace, need, q, qo_bytes))
+    return fail(FA_ERR_INVALID_ARG, "outputs or workspace alias inputs or each other");
+
+  const SplitPlan p = plan_splits(B, Hkv, max_seqlen_k);
+  const int64_t slots = (int64_t)B * Hq * p.max_splits;
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_offset_bytes(slots, d))
+                             : nullptr;
+  fa::DecodeArgs a{q, k_cache, v_cache, cu_seqlens_k, o, lse, part_o, part_lse, B, Hq, Hkv, d,
+                   p.max_splits, p.chunk, scale, reinterpret_cast<hipStream_t>(stream)};
+  const hipError_t e = fa::launch_decode_bf16(a);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -1,0 +1,100 @@
+// fa_common.h -- device-side helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// log2(e) and ln(2) as fp32 values; the kernels work in the base-2 exponent
+// domain (p = 2^(s*scale*log2e - m)) and convert LSE back to natural log.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// MI355X dispatches workgroup b to XCD (b mod 8).  Grids are padded to a
+// multiple of 8 and this maps the hardware id to a logical work index such
+// that each XCD receives one contiguous range of logical work (and so keeps
+// the K/V that range shares in its own L2).
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks_padded) {
+  const int per_xcd = nblocks_padded >> 3;
+  return (bid & 7) * per_xcd + (bid >> 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32;
+// `lo` lands in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// acc + lo + hi of a packed bf16 pair (one v_dot2 against (1, 1)).  Callers
+// pass scalar words: extracting the words from a vector first is avoided on
+// purpose (the compiler folds such extracts feeding v_dot2 into word 0).
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
+// Eight fp32 -> bf16x8 MFMA operand; *sum += the eight rounded values.
+__device__ __forceinline__ bf16x8 pack_bf16x8_sum(const float* f, float* sum) {
+  const uint32_t w0 = pack_bf16x2(f[0], f[1]);
+  const uint32_t w1 = pack_bf16x2(f[2], f[3]);
+  const uint32_t w2 = pack_bf16x2(f[4], f[5]);
+  const uint32_t w3 = pack_bf16x2(f[6], f[7]);
+  *sum = add_bf16x2(w3, add_bf16x2(w2, add_bf16x2(w1, add_bf16x2(w0, *sum))));
+  const u32x4 w = {w0, w1, w2, w3};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// (and DMA writes of such lanes into LDS write 0), so tile loads need no
+// per-lane bounds branches.  Word 3 is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from the buffer straight into LDS: lane l of the wave
+// writes lds_wave_base + 16*l (lds_wave_base must be wave-uniform).
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                                     lds_void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, byte_off, 0, 0, 0);
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// buffer->LDS copies) have completed: s_waitcnt vmcnt(0).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane r receives element j
+// (j = 0..3) from offset r%4 of the 8-byte row addressed by lane 4j + r/4.
+// `p` must point into LDS (a __shared__ array).
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
+
+}  // namespace fa

@@ -34,6 +34,10 @@ _ERRORS = {1: "invalid argument", 2: "softmax row sum differs from 1 by more tha
 
 _default = None
 
+# Worker threads when the caller does not say: the CPUs this process may use,
+# capped at 16 (the host share of one GPU on a shared node).
+DEFAULT_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+
 
 def compile_source(src: str, out: str) -> str:
     """Compile an oracle C source into a shared library with gcc (fp64, no fast-math)."""
@@ -99,6 +103,10 @@ def _ptr(a: np.ndarray):
     return ctypes.c_void_p(a.ctypes.data)
 
 
+def _threads(n: int) -> int:
+    return int(n) if n and n > 0 else DEFAULT_THREADS
+
+
 def _check(rc: int):
     if rc != 0:
         raise RuntimeError("oracle failed: " + _ERRORS.get(rc, "code %d" % rc))
@@ -129,7 +137,7 @@ def attention_rows(q, k, v, causal: bool, scale: float, rows, nthreads: int = 0,
     lse = np.zeros((R,), dtype=np.float64)
     rc = (lib or _load()).oracle_attn_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), B, Hq, Hkv, N, Nk, d,
                                   1 if causal else 0, float(scale), R, _ptr(rb), _ptr(rh),
-                                  _ptr(ri), _ptr(o), _ptr(lse), int(nthreads))
+                                  _ptr(ri), _ptr(o), _ptr(lse), _threads(nthreads))
     _check(rc)
     return o, lse
 
@@ -172,7 +180,7 @@ def decode_rows(q, k_cache, v_cache, cu_seqlens, scale: float, rows, nthreads: i
     lse = np.zeros((R,), dtype=np.float64)
     rc = (lib or _load()).oracle_decode_rows(dt, _ptr(qa), _ptr(ka), _ptr(va), _ptr(cu), B, Hq, Hkv, d,
                                     float(scale), R, _ptr(rb), _ptr(rh), _ptr(o), _ptr(lse),
-                                    int(nthreads))
+                                    _threads(nthreads))
     _check(rc)
     return o, lse
 

@@ -1,0 +1,142 @@
+"""The C ABI of libfa.so without a GPU: every symbol include/fa.h declares is
+exported, and argument errors are reported as status codes before anything is
+enqueued (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_fa_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+F32, BF16 = 0, 1
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def _no_gpu():
+    try:
+        import torch
+        return not torch.cuda.is_available()
+    except Exception:
+        return True
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+              "fa_last_error", "fa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(fa_lib):
+    raw = ctypes.CDLL(binding.library_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), "libfa.so does not export %s" % name
+
+
+def test_abi_version_and_status_names(fa_lib):
+    assert fa_lib.fa_abi_version() == 1
+    names = [fa_lib.fa_status_str(s).decode() for s in range(5)]
+    assert names == ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
+                     "FA_ERR_HIP"]
+    assert fa_lib.fa_status_str(99).decode() == "FA_ERR_UNKNOWN"
+
+
+def _fwd(lib, dtype=BF16, q=None, k=None, v=None, o=None, lse=None, B=1, Hq=2, Hkv=1, N=4, Nk=4,
+         d=64, causal=0, scale=0.125):
+    return lib.fa_fwd(dtype, q, k, v, o, lse, B, Hq, Hkv, N, Nk, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=7), FA_ERR_INVALID_ARG),
+    (dict(B=-1), FA_ERR_INVALID_ARG),
+    (dict(N=-3), FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), FA_ERR_INVALID_ARG),
+    (dict(Hq=0), FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), FA_ERR_INVALID_ARG),
+    (dict(d=0), FA_ERR_INVALID_ARG),
+    (dict(d=96), FA_ERR_UNSUPPORTED),
+    (dict(d=256), FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), FA_ERR_INVALID_ARG),
+    (dict(scale=-0.5), FA_ERR_INVALID_ARG),
+    (dict(), FA_ERR_INVALID_ARG),                       # null pointers with work to do
+    (dict(B=0), FA_OK),                                  # no work: nothing touched
+    (dict(N=0), FA_OK),
+])
+def test_fwd_validation(fa_lib, kwargs, status):
+    st = _fwd(fa_lib, **kwargs)
+    assert st == status
+    if status != FA_OK:
+        assert fa_lib.fa_last_error().decode() != ""
+    else:
+        assert fa_lib.fa_last_error().decode() == ""
+
+
+def _decode(lib, dtype=BF16, ptr=None, cu=None, max_len=100, B=2, Hq=8, Hkv=1, d=128,
+            scale=0.1, ws=None, ws_bytes=0):
+    return lib.fa_decode(dtype, ptr, ptr, ptr, cu, max_len, ptr, ptr, B, Hq, Hkv, d, scale, ws,
+                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=F32), FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), FA_ERR_INVALID_ARG),
+    (dict(B=-1), FA_ERR_INVALID_ARG),
+    (dict(max_len=-1), FA_ERR_INVALID_ARG),
+    (dict(Hq=8, Hkv=3), FA_ERR_INVALID_ARG),
+    (dict(Hq=32, Hkv=1), FA_ERR_UNSUPPORTED),           # group of 32 query heads
+    (dict(d=80), FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), FA_ERR_INVALID_ARG),
+    (dict(), FA_ERR_INVALID_ARG),                        # null pointers
+    (dict(B=0), FA_OK),
+])
+def test_decode_validation(fa_lib, kwargs, status):
+    assert _decode(fa_lib, **kwargs) == status
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device addresses; CPU-only check")
+def test_misaligned_and_aliased_pointers_rejected(fa_lib):
+    a, b2, c, o, lse = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+    st = fa_lib.fa_fwd(BF16, a + 2, b2, c, o, lse, 1, 2, 1, 4, 4, 64, 0, 0.125, None)
+    assert st == FA_ERR_INVALID_ARG and "aligned" in fa_lib.fa_last_error().decode()
+    st = fa_lib.fa_fwd(BF16, a, b2, c, a, lse, 1, 2, 1, 4, 4, 64, 0, 0.125, None)   # o == q
+    assert st == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device addresses; CPU-only check")
+def test_decode_workspace_checked(fa_lib):
+    need = fa_lib.fa_decode_workspace_bytes(2, 8, 1, 128, 100)
+    assert need > 0
+    p, cu, ws = 0x100000, 0x200000, 0x300000
+    st = _decode(fa_lib, ptr=p, cu=cu, ws=ws, ws_bytes=need - 1)
+    assert st == FA_ERR_WORKSPACE
+    st = _decode(fa_lib, ptr=p, cu=cu, ws=None, ws_bytes=need)
+    assert st == FA_ERR_WORKSPACE
+
+
+def test_workspace_size_query(fa_lib):
+    f = fa_lib.fa_decode_workspace_bytes
+    assert f(0, 64, 8, 128, 1000) == 0
+    assert f(32, 64, 8, 128, 0) == 0
+    small, large = f(32, 64, 8, 128, 512), f(32, 64, 8, 128, 32768)
+    assert 0 < small <= large
+    # partial outputs (fp32, d per slot) plus one fp32 LSE per slot
+    assert large < 32 * 64 * 128 * 4 * 64
+
+
+def test_binding_refuses_cpu_tensors(fa_lib):
+    import torch
+    q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous(), False, 0.125)

@@ -1,0 +1,313 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Tolerances (max abs error against the fp64 oracle): fp32 inputs 1e-5 on O and
+LSE; bf16 inputs 1e-2 on O and 1e-3 on LSE.  LSE = -inf on both sides counts as
+equal; any NaN fails.  Masking and cache indexing are checked bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_fa_amd import binding, inputs
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-5, 1e-5), torch.bfloat16: (1e-2, 1e-3)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    binding.load_library()          # raises if libfa.so is missing: no fallback path
+    yield
+    torch.cuda.synchronize()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def gpu_fwd(q, k, v, causal, scale):
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o, lse = binding.fwd(qd, kd, vd, causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def gpu_decode(q, kc, vc, cu, max_len, scale):
+    o, lse = binding.decode(q.cuda(), kc.cuda(), vc.cuda(), cu.cuda(), max_len, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def assert_close(got, ref, tol, what, rel=0.0):
+    """max |got - ref| <= tol + rel*|ref| elementwise (rel = 0 for the stated tolerances)."""
+    got = np.asarray(got.double() if torch.is_tensor(got) else got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert not np.isnan(got).any(), "%s: NaN in GPU output" % what
+    same_inf = np.isinf(got) & np.isinf(ref) & (np.sign(got) == np.sign(ref))
+    with np.errstate(invalid="ignore"):
+        err = np.where(same_inf, 0.0, np.abs(got - ref) - rel * np.abs(ref))
+    worst = float(err.max(initial=0.0))
+    _say("  %s: max abs err %.3g (tol %.1g)" % (what, worst, tol))
+    assert worst <= tol, "%s: max abs err %g > %g at %s" % (what, worst, tol,
+                                                             np.unravel_index(err.argmax(), err.shape))
+
+
+def check_full(q, k, v, causal, scale):
+    o, lse = gpu_fwd(q, k, v, causal, scale)
+    ro, rlse = oracle.attention(q, k, v, causal, scale)
+    tol_o, tol_l = TOL[q.dtype]
+    assert_close(o, ro, tol_o, "O")
+    assert_close(lse, rlse, tol_l, "LSE")
+    return o, lse
+
+
+# ------------------------------------------------------------------ workloads
+
+def test_workload_single_head_fp32():
+    cfg = inputs.SINGLE_HEAD_F32
+    _say("case: %s" % cfg.name)
+    check_full(*inputs.prefill_config_inputs(cfg), cfg.causal, cfg.scale)
+
+
+def test_workload_bert_large_bf16():
+    cfg = inputs.BERT_LARGE_BF16
+    _say("case: %s" % cfg.name)
+    check_full(*inputs.prefill_config_inputs(cfg), cfg.causal, cfg.scale)
+
+
+def test_workload_gpt2_causal_bf16():
+    cfg = inputs.GPT2_CAUSAL_BF16
+    _say("case: %s" % cfg.name)
+    check_full(*inputs.prefill_config_inputs(cfg), cfg.causal, cfg.scale)
+
+
+def _c4_rows(cfg, rng):
+    heads = [0, 1, 7, 8, 31, 56, 63]
+    fixed = [0, 1, 31, 32, 63, 64, 255, 256, 257, 1023, 4095, 4096, 8127, 8128, 8190, 8191]
+    rows = [(0, h, i) for h in heads for i in fixed]
+    rows += [(0, int(rng.integers(cfg.Hq)), int(rng.integers(cfg.N))) for _ in range(64)]
+    return np.array(rows)
+
+
+def test_workload_llama70b_gqa_full_size_sampled():
+    """Full-size launch (the one the benchmark times); the oracle checks a
+    sample of rows one by one and properties hold on every row."""
+    cfg = inputs.LLAMA70B_GQA_BF16
+    _say("case: %s (sampled rows)" % cfg.name)
+    q, k, v = inputs.prefill_config_inputs(cfg)
+    o, lse = gpu_fwd(q, k, v, cfg.causal, cfg.scale)
+    rows = _c4_rows(cfg, np.random.default_rng(0))
+    ro, rl = oracle.attention_rows(q, k, v, cfg.causal, cfg.scale, rows)
+    got_o = o[rows[:, 0], rows[:, 2], rows[:, 1]]
+    got_l = lse[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert_close(got_o, ro, 1e-2, "O (sampled rows)")
+    assert_close(got_l, rl, 1e-3, "LSE (sampled rows)")
+    # every row: finite, O inside the per-column range of V (a convex combination)
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    G = cfg.Hq // cfg.Hkv
+    vmin = v.float().amin(dim=1).repeat_interleave(G, dim=1)     # [B, Hq, d]
+    vmax = v.float().amax(dim=1).repeat_interleave(G, dim=1)
+    of = o.float()
+    assert (of >= vmin[:, None] - 1e-2).all() and (of <= vmax[:, None] + 1e-2).all()
+    # causal row 0 sees only key 0: O = V[0] bit for bit, in every head
+    assert torch.equal(o[:, 0], v[:, 0].repeat_interleave(G, dim=1))
+
+
+def test_workload_decode_full_size_sampled():
+    cfg = inputs.DECODE_VARLEN_BF16
+    _say("case: %s (sampled heads)" % cfg.name)
+    q, kc, vc, cu, lens = inputs.decode_config_inputs(cfg)
+    o, lse = gpu_decode(q, kc, vc, cu, int(lens.max()), cfg.scale)
+    rows = np.array([(b, h) for b in range(cfg.B) for h in (0, 9, 63)])
+    ro, rl = oracle.decode_rows(q, kc, vc, cu, cfg.scale, rows)
+    assert_close(o[rows[:, 0], rows[:, 1]], ro, 1e-2, "O (sampled)")
+    assert_close(lse[rows[:, 0], rows[:, 1]], rl, 1e-3, "LSE (sampled)")
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+
+
+# ------------------------------------------------------------- shape sweep
+
+SHAPES = [
+    # (B, Hq, Hkv, N, Nk)
+    (2, 4, 2, 300, 300),        # several tiles and a ragged tail
+    (1, 8, 1, 77, 530),         # N < Nk: bottom-right causal, group of 8
+    (1, 2, 2, 530, 77),         # N > Nk: leading causal rows see no key
+    (3, 2, 1, 1, 1),
+    (1, 1, 1, 1, 700),
+    (2, 16, 16, 257, 257),
+    (1, 4, 4, 513, 64),
+    (1, 2, 1, 64, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B%dHq%dHkv%dN%dNk%d" % s)
+def test_prefill_shapes(shape, causal, d, dtype):
+    B, Hq, Hkv, N, Nk = shape
+    _say("case: prefill %s causal=%s d=%d %s" % (shape, causal, d, dtype))
+    q, k, v = inputs.prefill_inputs(B, N, Nk, Hq, Hkv, d, dtype, seed=N + Nk + d)
+    check_full(q, k, v, causal, inputs.fp32_scale(d))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_peaked_softmax_rows(dtype):
+    """Q scaled by 10: scores spread over about +-30, the running max moves
+    often and most weights underflow.  Rows are then dominated by one key, so
+    |O| reaches the size of single V entries (up to ~5); rounding O to bf16
+    alone costs up to 2^-8 |O| there, which the bf16 bound adds to 1e-2.  In
+    fp32 the rounding error of a logit grows with its size, so ten times larger
+    logits get ten times the 1e-5 bound."""
+    _say("case: peaked softmax %s" % dtype)
+    q, k, v = inputs.prefill_inputs(2, 333, 333, 4, 2, 128, dtype, seed=7, q_mult=10.0)
+    tol_o, tol_l = TOL[dtype]
+    if dtype == torch.float32:
+        tol_o, tol_l = 10 * tol_o, 10 * tol_l
+    rel = 2.0 ** -8 if dtype == torch.bfloat16 else 0.0
+    for causal in (False, True):
+        o, lse = gpu_fwd(q, k, v, causal, inputs.fp32_scale(128))
+        ro, rl = oracle.attention(q, k, v, causal, inputs.fp32_scale(128))
+        assert_close(o, ro, tol_o, "O", rel=rel)
+        assert_close(lse, rl, tol_l, "LSE")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_no_keys_gives_zero_and_minus_inf(dtype):
+    q, k, v = inputs.prefill_inputs(2, 5, 0, 2, 1, 64, dtype)
+    o, lse = gpu_fwd(q, k, v, False, 0.125)
+    assert torch.equal(o, torch.zeros_like(o)) and bool((lse == -math.inf).all())
+
+
+def test_empty_batch_and_rows_are_noops():
+    for B, N in ((0, 16), (2, 0)):
+        q, k, v = inputs.prefill_inputs(B, N, 16, 2, 1, 64, torch.bfloat16)
+        o, lse = gpu_fwd(q, k, v, True, 0.125)
+        assert o.numel() == 0 and lse.numel() == 0
+
+
+# ----------------------------------------------------------- bitwise pins
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_masked_keys_have_no_effect_bitwise(dtype, d):
+    """Causal: rows <= r never see keys > r, so replacing those K/V rows with
+    other finite values leaves rows <= r unchanged bit for bit."""
+    B, Hq, Hkv, N = 1, 4, 2, 300
+    q, k, v = inputs.prefill_inputs(B, N, N, Hq, Hkv, d, dtype, seed=3)
+    o1, l1 = gpu_fwd(q, k, v, True, inputs.fp32_scale(d))
+    r = 137
+    k2, v2 = k.clone(), v.clone()
+    g = torch.Generator().manual_seed(99)
+    k2[:, r + 1:] = (torch.randn(k2[:, r + 1:].shape, generator=g) * 3).to(dtype)
+    v2[:, r + 1:] = (torch.randn(v2[:, r + 1:].shape, generator=g) * 3).to(dtype)
+    o2, l2 = gpu_fwd(q, k2, v2, True, inputs.fp32_scale(d))
+    assert torch.equal(o1[:, :r + 1], o2[:, :r + 1])
+    assert torch.equal(l1[:, :, :r + 1], l2[:, :, :r + 1])
+    assert not torch.equal(o1[:, r + 1:], o2[:, r + 1:])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_first_causal_row_returns_v0_bitwise(dtype):
+    q, k, v = inputs.prefill_inputs(2, 129, 129, 8, 2, 128, dtype, seed=4)
+    o, lse = gpu_fwd(q, k, v, True, inputs.fp32_scale(128))
+    assert torch.equal(o[:, 0], v[:, 0].repeat_interleave(4, dim=1))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_visible_key_count_is_exact(dtype):
+    """Q = 0: every visible score is 0, so LSE_i = ln(#visible keys); an
+    off-by-one in the mask moves LSE by at least 1/Nk."""
+    for N, Nk in ((300, 300), (100, 333)):
+        q = torch.zeros(1, N, 2, 64, dtype=dtype)
+        _, k, v = inputs.prefill_inputs(1, N, Nk, 2, 2, 64, dtype, seed=5)
+        _, lse = gpu_fwd(q, k, v, True, 0.125)
+        expect = torch.log(torch.arange(1, N + 1, dtype=torch.float64) + (Nk - N))
+        assert (lse.double() - expect).abs().max() <= 1e-5
+        _, lse = gpu_fwd(q, k, v, False, 0.125)
+        assert (lse.double() - math.log(Nk)).abs().max() <= 1e-5
+
+
+def test_gqa_equals_repeated_kv_heads_bitwise():
+    q, k, v = inputs.prefill_inputs(1, 200, 200, 16, 2, 128, torch.bfloat16, seed=6)
+    for causal in (False, True):
+        o1, l1 = gpu_fwd(q, k, v, causal, inputs.fp32_scale(128))
+        o2, l2 = gpu_fwd(q, k.repeat_interleave(8, dim=2).contiguous(),
+                         v.repeat_interleave(8, dim=2).contiguous(), causal, inputs.fp32_scale(128))
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeated_runs_are_bitwise_identical():
+    q, k, v = inputs.prefill_inputs(1, 1000, 1000, 8, 1, 128, torch.bfloat16, seed=8)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    ref = binding.fwd(qd, kd, vd, True, inputs.fp32_scale(128))
+    for _ in range(5):
+        o, lse = binding.fwd(qd, kd, vd, True, inputs.fp32_scale(128))
+        assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1])
+
+
+# ----------------------------------------------------------------- decode
+
+DECODE_CASES = [
+    # (lens, Hq, Hkv, d)
+    ([1, 7, 64, 65, 255, 256, 257, 1000, 3000, 0, 5000], 64, 8, 128),
+    ([1, 7, 64, 65, 255, 256, 257, 1000, 3000, 0, 5000], 32, 4, 64),
+    ([300, 1, 2049], 16, 1, 128),
+    ([33, 4100], 4, 4, 128),
+    ([0, 0, 0], 8, 8, 64),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=lambda c: "Hq%dHkv%dd%d" % c[1:])
+def test_decode_shapes(case):
+    lens, Hq, Hkv, d = case
+    _say("case: decode lens=%s Hq=%d Hkv=%d d=%d" % case)
+    q, kc, vc, cu = inputs.decode_inputs(lens, Hq, Hkv, d, torch.bfloat16, seed=len(lens) + d)
+    for max_len in (max(lens), max(lens) + 777):
+        o, lse = gpu_decode(q, kc, vc, cu, max_len, inputs.fp32_scale(d))
+        ro, rl = oracle.decode(q, kc, vc, cu, inputs.fp32_scale(d))
+        assert_close(o, ro, 1e-2, "O")
+        assert_close(lse, rl, 1e-3, "LSE")
+
+
+def test_decode_other_sequences_have_no_effect_bitwise():
+    lens = [900, 1500, 700]
+    q, kc, vc, cu = inputs.decode_inputs(lens, 64, 8, 128, torch.bfloat16, seed=10)
+    o1, l1 = gpu_decode(q, kc, vc, cu, 1500, inputs.fp32_scale(128))
+    kc2, vc2 = kc.clone(), vc.clone()
+    g = torch.Generator().manual_seed(1)
+    s, e = int(cu[1]), int(cu[2])
+    kc2[s:e] = (torch.randn(kc2[s:e].shape, generator=g) * 2).to(torch.bfloat16)
+    vc2[s:e] = (torch.randn(vc2[s:e].shape, generator=g) * 2).to(torch.bfloat16)
+    o2, l2 = gpu_decode(q, kc2, vc2, cu, 1500, inputs.fp32_scale(128))
+    for b in (0, 2):
+        assert torch.equal(o1[b], o2[b]) and torch.equal(l1[b], l2[b])
+    assert not torch.equal(o1[1], o2[1])
+
+
+def test_decode_visible_count_is_exact():
+    lens = [1, 513, 2048, 7777]
+    q, kc, vc, cu = inputs.decode_inputs(lens, 16, 2, 128, torch.bfloat16, seed=11)
+    q.zero_()
+    _, lse = gpu_decode(q, kc, vc, cu, 7777, 0.1)
+    expect = torch.log(torch.tensor(lens, dtype=torch.float64))[:, None]
+    assert (lse.double() - expect).abs().max() <= 1e-5
+
+
+def test_decode_matches_single_query_prefill():
+    lens = [700, 1300]
+    q, kc, vc, cu = inputs.decode_inputs(lens, 16, 2, 128, torch.bfloat16, seed=12)
+    o, lse = gpu_decode(q, kc, vc, cu, 1300, inputs.fp32_scale(128))
+    for b, L in enumerate(lens):
+        s = int(cu[b])
+        op, lp = gpu_fwd(q[b:b + 1, None].contiguous(), kc[None, s:s + L].contiguous(),
+                         vc[None, s:s + L].contiguous(), False, inputs.fp32_scale(128))
+        assert (o[b].float() - op[0, 0].float()).abs().max() <= 1e-2
+        assert (lse[b] - lp[0, :, 0]).abs().max() <= 1e-3

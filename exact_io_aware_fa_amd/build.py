@@ -28,9 +28,7 @@ HOST_SOURCES = ["fa_api.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 # Packed fp32 VALU instructions stay disabled for all device code.
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # keep MFMA accumulators in VGPRs (the softmax and rescale read them)
-          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc() -> str:

@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float mt = mx * c;
     const bool need = mt > m_ref + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
       const float m_new = need ? mt : m_ref;
       const float alpha = need ? fast_exp2(m_ref - m_new) : 1.0f;
       m_ref = m_new;

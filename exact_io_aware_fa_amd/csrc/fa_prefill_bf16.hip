@@ -12,11 +12,10 @@
 // second item).
 //
 // gfx950 mapping
-//  * workgroup = 4 waves = 256 query rows of one (batch, query head); a KV
-//    tile is 64 keys.  Wave w owns the 32-row query blocks w and 7-w of the
-//    workgroup, which balances causal work across the four waves.  64 query
-//    rows per wave keep LDS traffic at about half of the ~128 B/clk/CU the
-//    LDS delivers while the MFMA pipes are busy.
+//  * workgroup = 8 waves = 256 query rows of one (batch, query head); a KV
+//    tile is 64 keys and is shared by all 8 waves.  Wave w owns query rows
+//    32w..32w+31.  With ~170 registers per wave two waves share each SIMD, so
+//    one wave's softmax (VALU) runs while the other's MFMAs issue.
 //  * K and V tiles go from HBM straight into LDS with buffer_load ... lds
 //    (no staging registers); rows past the end of the sequence read as zero.
 //    Tile j+1 is in flight while tile j is computed (two LDS stages, one
@@ -44,6 +43,8 @@
 //    kRescaleSlack (so p <= 2^kRescaleSlack); any consistent reference gives
 //    the same O = sum p v / sum p.  The rescale of O is skipped for the whole
 //    wave when no row needs it.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -52,7 +53,8 @@ namespace {
 
 constexpr int kBR = 256;            // query rows per workgroup
 constexpr int kBC = 64;             // keys per KV tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr float kRescaleSlack = 8.0f;
 
 // Accumulator row R of a 32x32 MFMA lives in lane half (R>>2)&1, item
@@ -76,7 +78,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int RPI = 1024 / (2 * D);       // rows per 1 KB wave DMA instruction
   constexpr int TILE_ELEMS = kBC * D;
-  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / 4;
+  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / kWaves;
+  static_assert(DMA_PER_WAVE >= 1, "each wave issues at least one DMA per tensor");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE_ELEMS];
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const int lane = tid & 63;
   const int li = lane & 31;
   const int hh = lane >> 5;
-  const int qbase[2] = {q0 + 32 * wave, q0 + 32 * (7 - wave)};
+  const int qbase = q0 + 32 * wave;
   const int offs = Nk - N;                                      // bottom-right causal offset
 
   // ---- buffer views: one (batch, head) slice each; reads past the end are 0
@@ -113,12 +116,11 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(v + ((int64_t)b * Nk * Hkv + g) * D, kv_bytes);
 
   // ---- Q tile -> registers (B operand of S^T = K Q^T); rows past N read 0
-  bf16x8 qf[2][DSTEPS];
+  bf16x8 qf[DSTEPS];
+  {
+    const uint32_t off = (uint32_t)(qbase + li) * q_row_bytes + hh * 16;
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const uint32_t off = (uint32_t)(qbase[x] + li) * q_row_bytes + hh * 16;
-#pragma unroll
-    for (int t = 0; t < DSTEPS; ++t) qf[x][t] = __builtin_bit_cast(bf16x8, buffer_load16(q_rsrc, off + t * 32));
+    for (int t = 0; t < DSTEPS; ++t) qf[t] = __builtin_bit_cast(bf16x8, buffer_load16(q_rsrc, off + t * 32));
   }
 
   // ---- number of KV tiles this workgroup needs
@@ -166,148 +168,128 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   }
 
   // ---- accumulators
-  f32x16 acc_o[2][DBLK];
+  f32x16 acc_o[DBLK];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-    for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[x][d][r] = 0.0f;
-  float m_ref[2] = {-INFINITY, -INFINITY};
-  float l_part[2] = {0.0f, 0.0f};     // sum of fp32 weights (this lane's keys)
-  float l_rnd[2] = {0.0f, 0.0f};      // sum of bf16-rounded weights
+    for (int r = 0; r < 16; ++r) acc_o[d][r] = 0.0f;
+  float m_ref = -INFINITY;
+  float l_part = 0.0f;     // sum of fp32 weights (this lane's keys)
+  float l_rnd = 0.0f;      // sum of bf16-rounded weights
 
   if (n_kv > 0) issue_tile(0, 0);
 
-  for (int j = 0; j < n_kv; ++j) {
-    const int st = j & 1;
-    const int j0 = j * kBC;
-    wait_vmem_all();
-    __syncthreads();                                  // tile j is in LDS; stage st^1 is free
-    if (j + 1 < n_kv) issue_tile(j + 1, st ^ 1);
-
-    // which (query block, key block) pairs are fully visible / fully masked
-    bool full[2][2], none[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kmin = j0 + kb * 32, kmax = kmin + 31;
-        full[x][kb] = kmax < Nk && (!CAUSAL || kmax <= qbase[x] + offs);
-        none[x][kb] = kmin >= Nk || (CAUSAL && kmin > qbase[x] + 31 + offs);
-      }
+  // One KV tile.  MASKED = the tile holds keys that some row of this wave
+  // must not see (causal diagonal or keys past Nk): every score then goes
+  // through the visibility select.  Otherwise the body is straight-line.
+  auto tile_step = [&](const int st, const int j0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
 
     // ---- S^T = K Q^T
     const char* kst = reinterpret_cast<const char*>(&sK[st][0]);
-    f32x16 s[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[x][kb][r] = 0.0f;
+    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      if (none[0][kb] && none[1][kb]) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
       for (int t = 0; t < DSTEPS; ++t) {
         const bf16x8 a = __builtin_bit_cast(bf16x8, load16(kst + kb * 32 * (2 * D) + (t >> 2) * 128 + k_off[t & 3]));
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-          if (!none[x][kb]) s[x][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[x][t], s[x][kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
+        // keep at most a few operand reads in flight (bounds register use)
+        if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // ---- online softmax (per lane: one query row, 32 of the tile's 64 keys)
-    bf16x8 pf[2][2][2];
+    if (MASKED) {
+      const int qi = qbase + li;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int qi = qbase[x] + li;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (none[x][kb]) continue;
-        if (!full[x][kb]) {
-          const int kfirst = j0 + kb * 32 + hh * 16;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kfirst + r;
-            const bool vis = key < Nk && (!CAUSAL || key <= qi + offs);
-            s[x][kb][r] = vis ? s[x][kb][r] : -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[x][kb][r]);
-      }
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float mt = mx * c;
-      const bool need = mt > m_ref[x] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float m_new = need ? mt : m_ref[x];
-        const float alpha = need ? fast_exp2(m_ref[x] - m_new) : 1.0f;
-        m_ref[x] = m_new;
-        l_part[x] *= alpha;
-        l_rnd[x] *= alpha;
-#pragma unroll
-        for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[x][d][r] *= alpha;
-      }
-      const float mu = m_ref[x] == -INFINITY ? 0.0f : m_ref[x];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (none[x][kb]) {
-          pf[x][kb][0] = pf[x][kb][1] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-          continue;
-        }
-        float p[16];
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(fmaf(s[x][kb][r], c, -mu));
-          lsum += p[r];
+          const int key = j0 + kb * 32 + hh * 16 + r;
+          const bool vis = key < Nk && (!CAUSAL || key <= qi + offs);
+          s[kb][r] = vis ? s[kb][r] : -INFINITY;
         }
-        pf[x][kb][0] = pack_bf16x8_sum(&p[0], &l_rnd[x]);
-        pf[x][kb][1] = pack_bf16x8_sum(&p[8], &l_rnd[x]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float mt = mx * c;
+    const bool need = mt > m_ref + kRescaleSlack;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+      const float m_new = need ? mt : m_ref;
+      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.0f;
+      m_ref = m_new;
+      l_part *= alpha;
+      l_rnd *= alpha;
+#pragma unroll
+      for (int d = 0; d < DBLK; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[d][r] *= alpha;
+    }
+    const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(s[kb][r], c, -mu));
+        l_part += p[r];
       }
-      l_part[x] += lsum;
+      pf[kb][0] = pack_bf16x8_sum(&p[0], &l_rnd);
+      pf[kb][1] = pack_bf16x8_sum(&p[8], &l_rnd);
     }
 
     // ---- O^T += V^T P^T
     const char* vst = reinterpret_cast<const char*>(&sV[st][0]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (none[0][kb] && none[1][kb]) continue;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int d = 0; d < DBLK; ++d) {
           const char* base = vst + (kb * 32 + u * 8) * (2 * D) + (d >> 1) * 128 + v_off[d & 1];
           const u32x2 lo = lds_read_tr16(base);
           const u32x2 hi = lds_read_tr16(base + 4 * (2 * D));
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-          for (int x = 0; x < 2; ++x)
-            if (!none[x][kb])
-              acc_o[x][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[x][kb][u], acc_o[x][d], 0, 0, 0);
+          acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][u], acc_o[d], 0, 0, 0);
+          if ((d & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
-      }
-    }
+  };
+
+  // keys j0..j0+63 are all visible to every row of this wave iff the tile
+  // ends before Nk and (causal) before the first row's diagonal
+  for (int j = 0; j < n_kv; ++j) {
+    const int st = j & 1;
+    const int j0 = j * kBC;
+    wait_vmem_all();
+    __syncthreads();                                  // tile j is in LDS; stage st^1 is free
+    if (j + 1 < n_kv) issue_tile(j + 1, st ^ 1);
+    const bool clean = j0 + kBC <= Nk && (!CAUSAL || j0 + kBC - 1 <= qbase + offs);
+    if (clean)
+      tile_step(st, j0, std::integral_constant<bool, false>());
+    else
+      tile_step(st, j0, std::integral_constant<bool, true>());
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
   // lane (i, hh) item r holds head-dim 32*d + 8*(r/4) + 4*hh + r%4
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const float lt = l_part[x] + wave_xor32(l_part[x]);
-    const float lr = l_rnd[x] + wave_xor32(l_rnd[x]);
-    const int row = qbase[x] + li;
+  {
+    const float lt = l_part + wave_xor32(l_part);
+    const float lr = l_rnd + wave_xor32(l_rnd);
+    const int row = qbase + li;
     const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
     if (row < N) {
       uint16_t* dst = o + ((int64_t)b * N + row) * ((int64_t)Hq * D) + (int64_t)h * D + hh * 4;
 #pragma unroll
       for (int d = 0; d < DBLK; ++d) {
-        const f32x16 a = acc_o[x][d];
+        const f32x16 a = acc_o[d];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           u32x2 w;
@@ -317,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
         }
       }
       if (hh == 0)
-        lse[((int64_t)b * Hq + h) * N + row] = lt > 0.0f ? (m_ref[x] + fast_log2(lt)) * kLn2 : -INFINITY;
+        lse[((int64_t)b * Hq + h) * N + row] = lt > 0.0f ? (m_ref + fast_log2(lt)) * kLn2 : -INFINITY;
     }
   }
 }

@@ -30,7 +30,8 @@ class FaError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_PKG, _LIBNAME)
+    """The in-tree build; FA_LIBRARY names another build of the same library."""
+    return os.environ.get("FA_LIBRARY") or os.path.join(_PKG, _LIBNAME)
 
 
 def load_library():

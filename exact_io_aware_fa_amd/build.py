@@ -38,8 +38,8 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, extra: list[str]) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, extra: list[str], build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = [hipcc()] + COMMON + extra + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -47,21 +47,26 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
+    """Compile and link the library into `out`; `defines` (NAME=VALUE strings)
+    override tuning constants of the kernels."""
+    build_dir = BUILD if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = ["-D" + d for d in defines]
     host = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")]
-    jobs = [(s, DEVICE) for s in HIP_SOURCES] + [(s, host) for s in HOST_SOURCES]
+    jobs = [(s, DEVICE + dflags) for s in HIP_SOURCES] + [(s, host) for s in HOST_SOURCES]
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        objs = list(ex.map(lambda j: _compile(*j), jobs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda j: _compile(j[0], j[1], build_dir), jobs))
+    LIB_OUT = out
+    tmp = LIB_OUT + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, LIB_OUT)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", LIB_OUT)
+    return LIB_OUT
 
 
 if __name__ == "__main__":

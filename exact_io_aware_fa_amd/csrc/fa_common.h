@@ -63,6 +63,18 @@ __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u3
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// max(x[l], x[l ^ 32]) without touching LDS: v_permlane32_swap_b32 a, b swaps
+// lanes 32..63 of a with lanes 0..31 of b, so with a = b = x, a and b hold the
+// two halves of the wave in opposite order.  (__shfl_xor goes through
+// ds_bpermute, an LDS instruction, and the compiler then waits for every
+// outstanding buffer->LDS copy first.)  The nops keep the VALU write of the
+// operands and the read of the results clear of the swap.
+__device__ __forceinline__ float max_xor32(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // (and DMA writes of such lanes into LDS write 0), so tile loads need no
 // per-lane bounds branches.  Word 3 is the gfx9-family raw-buffer format.
@@ -78,14 +90,40 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from the buffer straight into LDS: lane l of the wave
 // writes lds_wave_base + 16*l (lds_wave_base must be wave-uniform).
-__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+// The byte offset is voff (per lane) + soff (wave-uniform, an SGPR).
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                                      lds_void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, byte_off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, soff, 0, 0);
 }
 
-// Wait until this wave's outstanding vector-memory operations (including
-// buffer->LDS copies) have completed: s_waitcnt vmcnt(0).
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's vector-memory operations (including
+// buffer->LDS copies) are outstanding: s_waitcnt vmcnt(N), 0 <= N < 16.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  // the fence keeps the scheduler from hoisting the wait above register-only
+  // work that precedes it (it would then wait for the copies too early)
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+__device__ __forceinline__ void wait_vmem_all() { wait_vmem_le<0>(); }
+
+// Workgroup barrier without a memory fence.  __syncthreads() fences, which
+// makes every wave wait for all of its outstanding buffer->LDS copies at every
+// barrier; kernels that track their copies with wait_vmem_le use this one.
+// The empty asm statements keep the compiler from moving memory accesses
+// across it; LDS reads issued before it have been consumed (and so completed)
+// before the wave reaches it, which the lgkmcnt wait makes explicit.
+// The scheduling fences keep the instructions of a phase on their side of the
+// barrier (without them register-only work is moved across it freely).
+__device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt left open
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;

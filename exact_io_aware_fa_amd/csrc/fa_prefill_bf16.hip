@@ -13,36 +13,38 @@
 //
 // gfx950 mapping
 //  * workgroup = 8 waves = 256 query rows of one (batch, query head); a KV
-//    tile is 64 keys and is shared by all 8 waves.  Wave w owns query rows
-//    32w..32w+31.  With ~170 registers per wave two waves share each SIMD, so
-//    one wave's softmax (VALU) runs while the other's MFMAs issue.
-//  * K and V tiles go from HBM straight into LDS with buffer_load ... lds
-//    (no staging registers); rows past the end of the sequence read as zero.
-//    Tile j+1 is in flight while tile j is computed (two LDS stages, one
-//    barrier per tile).
+//    tile is 64 keys, shared by all 8 waves.  Wave w owns query rows
+//    32w..32w+31.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: K from LDS is the A operand, Q sits in
 //    registers as the B operand for the whole kernel.  Lane (i, h) then holds
-//    16 keys of query row i and lane i^32 the other 16, so the row max is an
-//    in-lane reduction plus one exchange with lane^32, and the row sum is
-//    kept per lane and exchanged once at the end.
+//    16 keys of query row i and lane i^32 the other 16.
 //  * K rows are fed to the MFMA permuted (pi32) so that lane half h holds keys
 //    h*16+0..15: the fp32 scores convert to bf16 in place and already form the
-//    B operand of O^T += V^T P^T.
-//  * V stays row-major in LDS; its A operand (8 consecutive keys of one
-//    head-dim column per lane) is read with ds_read_b64_tr_b16.
-//  * LDS rows are XOR-swizzled per 16-byte chunk so that the MFMA operand
-//    reads are free of bank conflicts; the DMA writes realise the swizzle by
-//    choosing which global chunk each lane fetches.
-//  * Two row sums are kept: the fp32 sum of the weights (for LSE) and the sum
-//    of the bf16-rounded weights the P.V MFMA actually multiplies (for the
-//    normalisation of O), so O is an exact convex combination of the rounded
-//    weights and the rounding of P does not bias it.
-//  * The softmax runs in the base-2 domain: p = 2^(s*c - m), c = scale*log2(e).
-//    The reference max m only moves when a tile's max exceeds it by more than
+//    B operand of O^T += V^T P^T.  V stays row-major in LDS and its A operand
+//    (8 consecutive keys of one head-dim column per lane) is read with
+//    ds_read_b64_tr_b16.
+//  * LDS rows are XOR-swizzled per 16-byte chunk; the swizzles were chosen by
+//    measuring both read patterns on gfx950.  K and V tiles reach LDS by
+//    buffer_load ... lds (no staging registers; rows past the end read 0).
+//  * Ping-pong schedule.  Waves w and w+4 share a SIMD and belong to
+//    different groups.  Per tile a wave runs an MFMA block (P.V of the
+//    previous tile, then S of this tile) and a VALU block (softmax of this
+//    tile).  Group 1 runs half a tile behind group 0, and workgroup barriers
+//    separate the phases, so in every phase one wave of each SIMD issues MFMAs
+//    while the other runs its softmax.
+//  * Only group 0 moves data: after the last LDS read of its MFMA block it
+//    issues the DMA of the next K tile and of the current V tile, and it
+//    waits for them at the end of the following phase.  Its softmax has no
+//    branches, and the rare rescale of O is applied at the start of the next
+//    MFMA block, so nothing between the DMA and its wait makes the compiler
+//    drain the copy early.
+//  * Softmax in the base-2 domain: p = 2^(s*c - m), c = scale*log2(e).  The
+//    reference max m moves only when a tile's max exceeds it by more than
 //    kRescaleSlack (so p <= 2^kRescaleSlack); any consistent reference gives
-//    the same O = sum p v / sum p.  The rescale of O is skipped for the whole
-//    wave when no row needs it.
+//    the same O = sum p v / sum p.  Two row sums are kept: fp32 weights (for
+//    LSE) and the bf16-rounded weights the MFMA multiplies (to normalise O,
+//    so the rounding of P does not bias O).
 #include <type_traits>
 
 #include "fa_common.h"
@@ -53,8 +55,8 @@ namespace {
 
 constexpr int kBR = 256;            // query rows per workgroup
 constexpr int kBC = 64;             // keys per KV tile
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
 constexpr float kRescaleSlack = 8.0f;
 
 // Accumulator row R of a 32x32 MFMA lives in lane half (R>>2)&1, item
@@ -62,11 +64,14 @@ constexpr float kRescaleSlack = 8.0f;
 // in item r of lane half h.
 __device__ __forceinline__ int pi32(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
-// Chunk swizzles (XOR on the 16-byte chunk index within a row).
-//  K: the eight rows one ds_read_b128 phase touches differ in row bits 0,1,4.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 2) & 4); }
-//  V: a 16-lane transpose read touches 4 consecutive rows, 32 bytes each.
-__device__ __forceinline__ int swz_v(int row) { return (row & 3) << 1; }
+// Chunk swizzles (XOR on the 16-byte chunk index within a row of CPR chunks),
+// chosen by measuring the two read patterns on gfx950:
+//  K (ds_read_b128 of rows pi32(m)): XOR with the row's low bits.
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) { return row & (CPR > 16 ? 15 : CPR - 1); }
+//  V (ds_read_b64_tr_b16: 4 consecutive rows, 32 bytes each per 16 lanes).
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << (CPR >= 16 ? 2 : 1); }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
@@ -78,8 +83,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   constexpr int CPR = D / 8;                // 16-byte chunks per row
   constexpr int RPI = 1024 / (2 * D);       // rows per 1 KB wave DMA instruction
   constexpr int TILE_ELEMS = kBC * D;
-  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / kWaves;
-  static_assert(DMA_PER_WAVE >= 1, "each wave issues at least one DMA per tensor");
+  constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / (kWaves / 2);   // issued by group 0
+  static_assert(DMA_PER_WAVE >= 1, "each issuing wave issues at least one DMA per tensor");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE_ELEMS];
   __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE_ELEMS];
@@ -123,117 +128,153 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     for (int t = 0; t < DSTEPS; ++t) qf[t] = __builtin_bit_cast(bf16x8, buffer_load16(q_rsrc, off + t * 32));
   }
 
-  // ---- number of KV tiles this workgroup needs
+  // ---- KV tiles this workgroup needs, and where this wave's masked suffix starts
   int n_kv = (Nk + kBC - 1) / kBC;
   if (CAUSAL) {
     const int last_key = min(q0 + kBR - 1, N - 1) + offs;
     n_kv = last_key < 0 ? 0 : min(n_kv, last_key / kBC + 1);
   }
+  // tile j needs no mask for this wave iff j*64 + 63 < Nk and, when causal,
+  // j*64 + 63 <= qbase + offs (the wave's first row sees the whole tile)
+  int n_clean = Nk / kBC;
+  if (CAUSAL) {
+    const int d0 = qbase + offs - (kBC - 1);
+    n_clean = min(n_clean, d0 < 0 ? 0 : d0 / kBC + 1);
+  }
+  n_clean = min(n_clean, n_kv);
 
-  // ---- DMA of one K/V tile into LDS stage `st`: each wave issues
-  // DMA_PER_WAVE 1 KB instructions per tensor; lane l of instruction n fills
-  // row n*RPI + l/CPR, physical chunk l%CPR.
-  const int dma_row_in = lane / CPR;
-  const int dma_pc = lane % CPR;
-  auto issue_tile = [&](int j, int st) {
-    const int j0 = j * kBC;
+  // ---- DMA of one K or V tile into LDS stage `st` by the 4 waves of group 0:
+  // lane l of 1 KB instruction n fills row n*RPI + l/CPR, physical chunk
+  // l%CPR.  The per-lane offsets are fixed for the whole kernel (the tile
+  // offset is the scalar soffset), so their registers are never reused: the
+  // compiler treats a DMA's address register as pending until the copy lands.
+  const int dma_wave = wave % (kWaves / 2);
+  uint32_t k_voff[DMA_PER_WAVE], v_voff[DMA_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i) {
-      const int n = wave * DMA_PER_WAVE + i;
-      const int row = n * RPI + dma_row_in;
-      const uint32_t key_off = (uint32_t)(j0 + row) * kv_row_bytes;
-      buffer_load16_to_lds(k_rsrc, key_off + (uint32_t)((dma_pc ^ swz_k(row)) * 16), (lds_void*)&sK[st][n * 512]);
-      buffer_load16_to_lds(v_rsrc, key_off + (uint32_t)((dma_pc ^ swz_v(row)) * 16), (lds_void*)&sV[st][n * 512]);
-    }
+  for (int i = 0; i < DMA_PER_WAVE; ++i) {
+    const int row = (dma_wave * DMA_PER_WAVE + i) * RPI + lane / CPR;
+    const int pc = lane % CPR;
+    k_voff[i] = (uint32_t)row * kv_row_bytes + (uint32_t)((pc ^ swz_k<CPR>(row)) * 16);
+    v_voff[i] = (uint32_t)row * kv_row_bytes + (uint32_t)((pc ^ swz_v<CPR>(row)) * 16);
+  }
+  auto issue_k = [&](int j, int st) {
+    const uint32_t tile_off = (uint32_t)(j * kBC) * kv_row_bytes;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      buffer_load16_to_lds(k_rsrc, k_voff[i], tile_off, (lds_void*)&sK[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
+  };
+  auto issue_v = [&](int j, int st) {
+    const uint32_t tile_off = (uint32_t)(j * kBC) * kv_row_bytes;
+#pragma unroll
+    for (int i = 0; i < DMA_PER_WAVE; ++i)
+      buffer_load16_to_lds(v_rsrc, v_voff[i], tile_off, (lds_void*)&sV[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
   };
 
   // ---- lane-constant LDS offsets (bytes) for the MFMA operand reads
-  // K (A operand of S^T): row kb*32 + pi32(li), chunk 2t + hh swizzled; for
-  // t = 4*t1 + t0 the swizzled chunk is 8*t1 + ((2*t0 + hh) ^ swz_k(row)).
+  // K (A operand of S^T): row kb*32 + pi32(li), logical chunk 2t + hh; the
+  // swizzle depends only on the row's low bits, so it is the same for kb = 0, 1.
   const int krow = pi32(li);
-  int k_off[4];
+  int k_off[DSTEPS];
 #pragma unroll
-  for (int t0 = 0; t0 < 4; ++t0) k_off[t0] = krow * (2 * D) + (((2 * t0 + hh) ^ swz_k(krow)) * 16);
+  for (int t = 0; t < DSTEPS; ++t) k_off[t] = krow * (2 * D) + (((2 * t + hh) ^ swz_k<CPR>(krow)) * 16);
   // V (A operand of O^T, transpose read): 16-lane group (mh, h) of the wave,
-  // lane r points at key  h*16 + r/4 (+ kb*32 + u*8 + 4*rho)  and head-dim
-  // 16*mh + 4*(r%4) (+ 32*ddb).
+  // lane r points at key h*16 + r/4 (+ kb*32 + u*8 + 4*rho) and head-dim
+  // 32*d + 16*mh + 4*(r%4).
   const int r16 = lane & 15;
   const int mh = (lane >> 4) & 1;
   const int vrow = hh * 16 + (r16 >> 2);
-  int v_off[2];
+  int v_off[DBLK];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int chunk = 4 * par + 2 * mh + ((r16 & 3) >> 1);
-    v_off[par] = vrow * (2 * D) + ((chunk ^ swz_v(vrow)) * 16) + (r16 & 1) * 8;
+  for (int d = 0; d < DBLK; ++d) {
+    const int chunk = 4 * d + 2 * mh + ((r16 & 3) >> 1);
+    v_off[d] = vrow * (2 * D) + ((chunk ^ swz_v<CPR>(vrow)) * 16) + (r16 & 1) * 8;
   }
 
-  // ---- accumulators
+  // ---- state
   f32x16 acc_o[DBLK];
 #pragma unroll
   for (int d = 0; d < DBLK; ++d)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[d][r] = 0.0f;
-  float m_ref = -INFINITY;
-  float l_part = 0.0f;     // sum of fp32 weights (this lane's keys)
-  float l_rnd = 0.0f;      // sum of bf16-rounded weights
+  float m_ref = -INFINITY;   // running reference max (base-2 domain), same in both lanes of a row
+  float l_part = 0.0f;       // sum of fp32 weights over this lane's keys
+  float l_rnd = 0.0f;        // sum of the bf16-rounded weights over this lane's keys
+  float alpha = 1.0f;        // pending rescale of acc_o (applied before the next P.V)
+  bool rescale = false;      // wave-uniform: some row of the wave has alpha != 1
+  f32x16 s[2];               // scores of the current tile (two 32-key blocks)
+  bf16x8 pf[2][2];           // weights of the current tile, B operands of P.V
 
-  if (n_kv > 0) issue_tile(0, 0);
-
-  // One KV tile.  MASKED = the tile holds keys that some row of this wave
-  // must not see (causal diagonal or keys past Nk): every score then goes
-  // through the visibility select.  Otherwise the body is straight-line.
-  auto tile_step = [&](const int st, const int j0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-
-    // ---- S^T = K Q^T
-    const char* kst = reinterpret_cast<const char*>(&sK[st][0]);
-    f32x16 s[2];
+  // S^T = K Q^T for the tile in K stage `kst_i`
+  auto stage_s = [&](const int kst_i) {
+    const char* kst = reinterpret_cast<const char*>(&sK[kst_i][0]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
       for (int t = 0; t < DSTEPS; ++t) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, load16(kst + kb * 32 * (2 * D) + (t >> 2) * 128 + k_off[t & 3]));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, load16(kst + kb * 32 * (2 * D) + k_off[t]));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[t], s[kb], 0, 0, 0);
         // keep at most a few operand reads in flight (bounds register use)
         if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
 
-    // ---- online softmax (per lane: one query row, 32 of the tile's 64 keys)
-    if (MASKED) {
-      const int qi = qbase + li;
+  // O^T = alpha*O^T + V^T P^T for the tile in V stage `vst_i`
+  auto stage_pv = [&](const int vst_i) {
+    if (__builtin_expect(rescale, 0)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int d = 0; d < DBLK; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + kb * 32 + hh * 16 + r;
-          const bool vis = key < Nk && (!CAUSAL || key <= qi + offs);
-          s[kb][r] = vis ? s[kb][r] : -INFINITY;
+        for (int r = 0; r < 16; ++r) acc_o[d][r] *= alpha;
+    }
+    const char* vst = reinterpret_cast<const char*>(&sV[vst_i][0]);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int d = 0; d < DBLK; ++d) {
+          const char* base = vst + (kb * 32 + u * 8) * (2 * D) + v_off[d];
+          const u32x2 lo = lds_read_tr16(base);
+          const u32x2 hi = lds_read_tr16(base + 4 * (2 * D));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][u], acc_o[d], 0, 0, 0);
+          if ((d & 3) == 3) __builtin_amdgcn_sched_barrier(0);
         }
+  };
+
+  // online softmax of the tile of keys j0..j0+63 -> pf, branch-free.  MASKED:
+  // some key of the tile is invisible to some row of this wave.
+  auto stage_softmax = [&](const int j0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if (MASKED) {
+      // last visible key of this lane's row; item r of block kb holds key
+      // j0 + kb*32 + hh*16 + r
+      const int lim = CAUSAL ? min(Nk - 1, qbase + li + offs) : Nk - 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int thr = lim - (j0 + kb * 32 + hh * 16);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = r <= thr ? s[kb][r] : -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
+    mx = max_xor32(mx);                        // the row's other 32 keys sit in lane^32
     const float mt = mx * c;
     const bool need = mt > m_ref + kRescaleSlack;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-      const float m_new = need ? mt : m_ref;
-      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.0f;
-      m_ref = m_new;
-      l_part *= alpha;
-      l_rnd *= alpha;
-#pragma unroll
-      for (int d = 0; d < DBLK; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[d][r] *= alpha;
-    }
+    const float m_new = need ? mt : m_ref;
+    alpha = need ? fast_exp2(m_ref - m_new) : 1.0f;   // 0 when m_ref was -inf
+    rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+    m_ref = m_new;
+    l_part *= alpha;
+    l_rnd *= alpha;
     const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
-    bf16x8 pf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
@@ -245,41 +286,58 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
       pf[kb][0] = pack_bf16x8_sum(&p[0], &l_rnd);
       pf[kb][1] = pack_bf16x8_sum(&p[8], &l_rnd);
     }
-
-    // ---- O^T += V^T P^T
-    const char* vst = reinterpret_cast<const char*>(&sV[st][0]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int d = 0; d < DBLK; ++d) {
-          const char* base = vst + (kb * 32 + u * 8) * (2 * D) + (d >> 1) * 128 + v_off[d & 1];
-          const u32x2 lo = lds_read_tr16(base);
-          const u32x2 hi = lds_read_tr16(base + 4 * (2 * D));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          acc_o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][u], acc_o[d], 0, 0, 0);
-          if ((d & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
   };
+  const auto kClean = std::integral_constant<bool, false>();
+  const auto kMasked = std::integral_constant<bool, true>();
 
-  // keys j0..j0+63 are all visible to every row of this wave iff the tile
-  // ends before Nk and (causal) before the first row's diagonal
-  for (int j = 0; j < n_kv; ++j) {
-    const int st = j & 1;
-    const int j0 = j * kBC;
-    wait_vmem_all();
-    __syncthreads();                                  // tile j is in LDS; stage st^1 is free
-    if (j + 1 < n_kv) issue_tile(j + 1, st ^ 1);
-    const bool clean = j0 + kBC <= Nk && (!CAUSAL || j0 + kBC - 1 <= qbase + offs);
-    if (clean)
-      tile_step(st, j0, std::integral_constant<bool, false>());
-    else
-      tile_step(st, j0, std::integral_constant<bool, true>());
+  // ---- ping-pong schedule.  Group g runs the MFMA block M_j = [P.V of tile
+  // j-1, S of tile j] in phase 2j+g and the softmax V_j in phase 2j+1+g;
+  // both groups execute 2*n_kv + 2 barriers.  Group 0 issues the DMA of
+  // K_{j+1} and V_j at the end of M_j (into the stages tile j-1 used) and
+  // waits for it at the end of phase 2j+1; both groups read them from phase
+  // 2j+2 on.
+  const int group = wave >= kWaves / 2 ? 1 : 0;
+  if (n_kv > 0) {
+    if (group == 0) {
+      issue_k(0, 0);
+      wait_vmem_all();
+    }
+    barrier_no_fence();
+    if (group == 0) {
+      auto step = [&](const int j, auto masked_tag) {
+        if (j >= 1) stage_pv((j - 1) & 1);          // phase 2j: M_j
+        stage_s(j & 1);
+        if (j + 1 < n_kv) issue_k(j + 1, (j + 1) & 1);
+        issue_v(j, j & 1);
+        barrier_no_fence();
+        stage_softmax(j * kBC, masked_tag);          // phase 2j+1: V_j
+        wait_vmem_all();
+        barrier_no_fence();
+      };
+      for (int j = 0; j < n_clean; ++j) step(j, kClean);
+      for (int j = n_clean; j < n_kv; ++j) step(j, kMasked);
+      stage_pv((n_kv - 1) & 1);                     // phase 2n: M_n
+      barrier_no_fence();
+      barrier_no_fence();                           // phase 2n+1: idle
+    } else {
+      barrier_no_fence();                           // phase 0: idle
+      auto step = [&](const int j, auto masked_tag) {
+        if (j >= 1) stage_pv((j - 1) & 1);          // phase 2j+1: M_j
+        stage_s(j & 1);
+        barrier_no_fence();
+        stage_softmax(j * kBC, masked_tag);          // phase 2j+2: V_j
+        barrier_no_fence();
+      };
+      for (int j = 0; j < n_clean; ++j) step(j, kClean);
+      for (int j = n_clean; j < n_kv; ++j) step(j, kMasked);
+      stage_pv((n_kv - 1) & 1);                     // phase 2n+1: M_n
+      barrier_no_fence();
+    }
   }
 
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = acc / l_rnd, LSE = (m + log2 l) * ln 2
   // lane (i, hh) item r holds head-dim 32*d + 8*(r/4) + 4*hh + r%4
+  // (the last tile's rescale was applied by the final P.V block)
   {
     const float lt = l_part + wave_xor32(l_part);
     const float lr = l_rnd + wave_xor32(l_rnd);

@@ -70,7 +70,7 @@ def decode_bytes(cfg, total_len):
 
 
 def cpu_baseline(q, k, v, cfg):
-    """The fp64 oracle on a bounded sample of the prefill workload: every 32nd
+    """The fp64 oracle on a bounded sample of the prefill workload: every 8th
     query row, all heads.  Reported as algorithmic TFLOP/s of the sample."""
     import numpy as np
     from oracle import oracle

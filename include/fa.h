@@ -27,9 +27,10 @@
  *  - Grouped-query attention: Hq must be a multiple of Hkv and query head h
  *    reads kv head h / (Hq / Hkv) (contiguous groups).
  *  - head dimension d must be 64 or 128.
- *  - scale must be finite.
- *  - The library keeps no mutable global state; calls on different streams
- *    may run concurrently.
+ *  - scale must be finite and positive.
+ *  - The only mutable state is a per-thread copy of the last error's detail
+ *    text (fa_last_error); calls from several threads and on different
+ *    streams may run concurrently.
  */
 #ifndef FA_H
 #define FA_H

@@ -22,7 +22,7 @@
  *  - effectstory.com page, section "What is FlashAttention": exact, not an
  *    approximation.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - causal alignment is bottom-right: key j is visible to query i iff
  *    j <= i + (Nk - N); with N == Nk this is j <= i;
  *  - LSE is the natural log of sum_j exp(S_ij) over visible keys, scale included;

@@ -54,7 +54,7 @@ def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
     os.makedirs(build_dir, exist_ok=True)
     dflags = ["-D" + d for d in defines]
     host = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROCM, "include")]
-    jobs = [(s, DEVICE + dflags) for s in HIP_SOURCES] + [(s, host) for s in HOST_SOURCES]
+    jobs = [(s, DEVICE + dflags) for s in HIP_SOURCES] + [(s, host + dflags) for s in HOST_SOURCES]
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile(j[0], j[1], build_dir), jobs))
     LIB_OUT = out

@@ -3,6 +3,7 @@
 // Nothing here touches the device before every argument has been checked.
 #include "fa.h"
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -39,33 +40,41 @@ bool overlaps(const void* p, size_t bytes, const void* r, size_t rbytes) {
   return a < c + rbytes && c < a + bytes;
 }
 
-// Decode split plan: every sequence's cache is cut into chunks of `chunk`
-// keys (a multiple of the kernel's 256-key granule); the grid aims at about
-// kTargetSplitBlocks workgroups when all caches are as long as the bound.
-constexpr int64_t kTargetSplitBlocks = 2048;
+// Decode work plan: the split kernel runs `waves` single-wave workgroups that
+// share the (sequence, kv head, key) units evenly.  About one and a half
+// rounds of resident waves (2 per SIMD on 256 CUs is 2048): every wave's share
+// is equal, a wave's start-up cost is paid few times, the partial results
+// stay at waves + B*Hkv slots, and a GPU that holds somewhat fewer waves at
+// once still finishes in two even rounds.  Fewer waves when the caches are
+// short, so that a wave gets at least kMinKeysPerWave keys.
+#ifndef FA_DECODE_WAVES
+#define FA_DECODE_WAVES 3072
+#endif
+constexpr int64_t kDecodeWaves = FA_DECODE_WAVES;
+constexpr int64_t kMinKeysPerWave = 256;
 
-struct SplitPlan {
-  int chunk;
-  int max_splits;
-};
-
-SplitPlan plan_splits(int B, int Hkv, int max_seqlen_k) {
-  const int granule = fa::decode_chunk_granule();
-  SplitPlan p{granule, 0};
-  if (B <= 0 || Hkv <= 0 || max_seqlen_k <= 0) return p;
-  int64_t per_seq = (kTargetSplitBlocks + (int64_t)B * Hkv - 1) / ((int64_t)B * Hkv);
-  if (per_seq < 1) per_seq = 1;
-  int64_t chunk = (max_seqlen_k + per_seq - 1) / per_seq;
-  chunk = (chunk + granule - 1) / granule * granule;
-  if (chunk < granule) chunk = granule;
-  p.chunk = (int)chunk;
-  p.max_splits = (int)((max_seqlen_k + chunk - 1) / chunk);
-  return p;
+int plan_waves(int B, int Hkv, int max_seqlen_k) {
+  if (B <= 0 || Hkv <= 0 || max_seqlen_k <= 0) return 0;
+  const int64_t units = (int64_t)B * Hkv * max_seqlen_k;
+  const int64_t w = (units + kMinKeysPerWave - 1) / kMinKeysPerWave;
+  return (int)std::min(kDecodeWaves, std::max<int64_t>(1, w));
 }
 
-size_t lse_offset_bytes(int64_t slots, int d) {
-  const size_t o_bytes = (size_t)slots * (size_t)d * sizeof(float);
-  return (o_bytes + 255) / 256 * 256;
+struct DecodeLayout {
+  int waves;
+  int64_t slots;          // partial-result slots: waves + B*Hkv, each G heads
+  size_t lse_offset;      // byte offset of part_lse in the workspace
+  size_t bytes;
+};
+
+DecodeLayout decode_layout(int B, int Hq, int Hkv, int d, int max_seqlen_k) {
+  DecodeLayout l{plan_waves(B, Hkv, max_seqlen_k), 0, 0, 0};
+  if (l.waves == 0) return l;
+  l.slots = (int64_t)l.waves + (int64_t)B * Hkv;
+  const int64_t rows = l.slots * (Hq / Hkv);
+  l.lse_offset = ((size_t)rows * d * sizeof(float) + 255) / 256 * 256;
+  l.bytes = l.lse_offset + (size_t)rows * sizeof(float);
+  return l;
 }
 
 }  // namespace
@@ -127,10 +136,8 @@ FA_EXPORT fa_status_t fa_fwd(fa_dtype_t dtype, const void* q, const void* k, con
 }
 
 FA_EXPORT size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen_k <= 0) return 0;
-  const SplitPlan p = plan_splits(B, Hkv, max_seqlen_k);
-  const int64_t slots = (int64_t)B * Hq * p.max_splits;
-  return lse_offset_bytes(slots, d) + (size_t)slots * sizeof(float);
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen_k <= 0 || Hq % Hkv != 0) return 0;
+  return decode_layout(B, Hq, Hkv, d, max_seqlen_k).bytes;
 }
 
 FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_cache, const void* v_cache,
@@ -167,13 +174,12 @@ FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_c
       overlaps(workspace, need, lse, lse_bytes) || overlaps(workspace, need, q, qo_bytes))
     return fail(FA_ERR_INVALID_ARG, "outputs or workspace alias inputs or each other");
 
-  const SplitPlan p = plan_splits(B, Hkv, max_seqlen_k);
-  const int64_t slots = (int64_t)B * Hq * p.max_splits;
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lse_offset_bytes(slots, d))
-                             : nullptr;
+  const DecodeLayout lay = decode_layout(B, Hq, Hkv, d, max_seqlen_k);
+  float* part_o = lay.waves > 0 ? static_cast<float*>(workspace) : nullptr;
+  float* part_lse =
+      lay.waves > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.lse_offset) : nullptr;
   fa::DecodeArgs a{q, k_cache, v_cache, cu_seqlens_k, o, lse, part_o, part_lse, B, Hq, Hkv, d,
-                   p.max_splits, p.chunk, scale, reinterpret_cast<hipStream_t>(stream)};
+                   lay.waves, scale, reinterpret_cast<hipStream_t>(stream)};
   const hipError_t e = fa::launch_decode_bf16(a);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

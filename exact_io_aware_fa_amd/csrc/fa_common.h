@@ -75,9 +75,20 @@ __device__ __forceinline__ float max_xor32(float x) {
   return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
 
+// The same for lanes l and l ^ 16: v_permlane16_swap_b32 a, b swaps the odd
+// 16-lane rows of a with the even rows of b.
+__device__ __forceinline__ float max_xor16(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // (and DMA writes of such lanes into LDS write 0), so tile loads need no
-// per-lane bounds branches.  Word 3 is the gfx9-family raw-buffer format.
+// per-lane bounds branches.  Only the per-lane (VGPR) offset is range
+// checked; the scalar offset of an access is not, so an offset that may run
+// past the end must go into the per-lane offset or into the base.  Word 3 is
+// the gfx9-family raw-buffer format.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
@@ -90,7 +101,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from the buffer straight into LDS: lane l of the wave
 // writes lds_wave_base + 16*l (lds_wave_base must be wave-uniform).
-// The byte offset is voff (per lane) + soff (wave-uniform, an SGPR).
+// The byte offset is voff (per lane, range checked) + soff (wave-uniform,
+// an SGPR, not range checked).
 __device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                                      lds_void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, soff, 0, 0);

@@ -4,290 +4,386 @@
 // One new query token per sequence attends to every row of that sequence's
 // cache; only the real cache length is read (ai6s.net page, section "what
 // ops-transformer adds", third item).  Work is split along the cache: each
-// workgroup reduces one chunk of one (sequence, kv head) with the online
+// wave reduces pieces of (sequence, kv head) key ranges with the online
 // softmax (ai6s.net page, section "FlashAttention changes the dataflow, not
-// the algorithm") and writes a partial output normalised by its own row sum
-// plus that chunk's logsumexp.  A second kernel merges the partials of a
-// sequence with weights exp(LSE_s - LSE), LSE = log sum_s exp(LSE_s), which is
-// the same rescaling the online softmax applies tile by tile.
+// the algorithm") and writes, per piece, a partial output normalised by its
+// own row sum plus the piece's logsumexp.  A second kernel merges the pieces
+// of a sequence with weights exp(LSE_s - LSE), LSE = log sum_s exp(LSE_s),
+// which is the same rescaling the online softmax applies tile by tile.
 //
-// gfx950 mapping (split kernel)
-//  * workgroup = 4 waves; wave w streams 64-key sub-tiles w, w+4, ... of the
-//    chunk.  All query heads of one kv group (G = Hq/Hkv <= 16) share each K/V
-//    byte, so K and V are read from HBM exactly once.
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K is loaded from HBM straight
-//    into A-operand registers (16-byte loads), Q^T (G heads padded to 16
-//    columns) is the B operand.  The K rows fed to each MFMA are permuted so
-//    that every lane ends up holding 8 consecutive keys of one query head,
-//    which is exactly its B-operand slice of the following P.V MFMA.
-//  * V is transposed through a per-wave LDS tile (4x8 register transpose,
-//    8-byte writes) and read back as 16-byte V^T A-operand slices.
-//  * The four waves' (max, sum, output) are merged through LDS at the end.
+// gfx950 mapping (split kernel).  The kernel streams the cache once and does
+// 8 flops per byte, so it is bound by HBM bandwidth.
+//  * Work is split evenly ("stream-K"): the units are the (sequence, kv head,
+//    key) triples in that order, K = total keys * Hkv of them, and wave w of W
+//    takes units [floor(w K / W), floor((w+1) K / W)).  Every wave streams the
+//    same number of cache rows whatever the mix of lengths, so the waves of a
+//    launch finish together; W spans a few rounds of resident waves.  A wave
+//    writes one partial result per (sequence, kv head) piece it covers.
+//  * workgroup = one wave; no barriers.  All G = Hq/Hkv <= 16 query heads of
+//    the kv head share every K/V byte, so the cache is read from HBM once.
+//  * A piece is streamed in 32-key tiles with two register sets: the loads of
+//    tile t+1 are issued before tile t is computed.  The buffer view ends at
+//    the piece's last row, so the ragged last tile (and the tile past the end
+//    that the pipeline loads) read 0 without touching memory.
+//  * K and V rows are loaded whole (4 rows of 256 bytes per instruction at
+//    d=128; loads that cover only part of a 128-byte line per row measurably
+//    lower the bandwidth of this strided layout) and stored row-major in
+//    per-wave LDS tiles, with 16-byte chunks XOR-swizzled by the row.
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: K slices are read back with
+//    ds_read_b128 as the A operand; Q^T (G heads padded to 16 columns) is the
+//    B operand.  Lane (head j, group c) then holds keys 4c..4c+3 and
+//    16+4c..16+4c+3 of the tile, which are exactly its slice of the B operand
+//    P^T of the following O^T += V^T P^T.
+//  * V^T, the A operand of that product, is read transposed from the V tile
+//    with ds_read_b64_tr_b16.
 #include "fa_common.h"
 #include "fa_kernels.h"
 
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kSub = 64;            // keys per wave sub-tile
-constexpr int kGMax = 16;           // query heads per kv head handled by one MFMA column block
+constexpr int kTile = 32;           // keys per tile
+constexpr int kGMax = 16;           // query heads per kv head (one MFMA column block)
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ int swz_d(int row) { return (row & 7) ^ ((row >> 3) & 7); }
+// Chunk swizzles (XOR on the 16-byte chunk index of a row of CPR chunks):
+//  K: the 16 rows of one A-operand read (same logical chunk) hit different banks;
+template <int CPR>
+__device__ __forceinline__ int swz_k(int row) { return row & (CPR - 1); }
+//  V: rows 4c..4c+3 of one transposed read land in different banks.
+template <int CPR>
+__device__ __forceinline__ int swz_v(int row) { return (row & 3) << (CPR >= 16 ? 2 : 1); }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ cu, float* __restrict__ part_o, float* __restrict__ part_lse, int Hq,
-    int Hkv, int max_splits, int chunk, float c) {
-  constexpr int DT = D / 32;          // MFMA k-steps of S^T
-  constexpr int DB = D / 16;          // 16-wide head-dim blocks of O^T
-  constexpr int KCH = D / 8;          // 16-byte chunks per row
-  constexpr int VIT = kSub * KCH / 4 / 64;   // 4-key x 8-dim blocks per lane
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[kWaves][D * kSub];
-  __shared__ float s_m[kWaves][kGMax], s_l[kWaves][kGMax], s_lr[kWaves][kGMax];
+struct KvTile {
+  u32x4 k[kTile * D * 2 / 1024];       // K rows, 1 KB per wave load
+  u32x4 v[kTile * D * 2 / 1024];       // V rows, 1 KB per wave load
+};
 
-  const int split = blockIdx.x % max_splits;
-  const int rest = blockIdx.x / max_splits;
-  const int g = rest % Hkv;
-  const int b = rest / Hkv;
-  const int start = cu[b];
-  const int L = cu[b + 1] - start;
-  const int ks = split * chunk;
-  if (ks >= L) return;                                 // past this sequence's cache
-  const int ke = min(L, ks + chunk);
-  const int G = Hq / Hkv;
+// ---- the even split.  bound(w) = floor(w K / W) is the first unit of wave w.
+__device__ __forceinline__ int64_t part_bound(int64_t w, int64_t K, int W) { return w * K / W; }
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-  const int lane = tid & 63;
-  const int l16 = lane & 15;
-  const int grp = lane >> 4;                           // 0..3
-  const int64_t row_stride = (int64_t)Hkv * D;
-  const uint16_t* kbase = kc + ((int64_t)start * Hkv + g) * D;
-  const uint16_t* vbase = vc + ((int64_t)start * Hkv + g) * D;
+// The wave whose units include u (0 <= u < K): the largest w with
+// bound(w) <= u, i.e. floor(((u+1) W - 1) / K); it is never an empty wave.
+__device__ __forceinline__ int wave_of(int64_t u, int64_t K, int W) {
+  return (int)(((u + 1) * W - 1) / K);
+}
 
-  // Q^T as B operand: column n = query head g*G + n (zero for n >= G)
-  bf16x8 qf[DT];
-  {
-    const bool valid = l16 < G;
-    const uint16_t* src = q + ((int64_t)b * Hq + g * G + (valid ? l16 : 0)) * D + grp * 8;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (valid) w = load16(src + t * 32);
-      qf[t] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
+// Partial-result slot of a piece: a piece that starts at its (sequence, kv
+// head)'s first key uses slot W + b*Hkv + g; a piece that continues one from
+// the previous wave (it starts at its wave's first unit) uses slot w.
+__device__ __forceinline__ int64_t piece_slot(bool first_key, int w, int W, int b, int Hkv, int g) {
+  return first_key ? (int64_t)W + (int64_t)b * Hkv + g : (int64_t)w;
+}
 
-  f32x4 acc[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY, l_part = 0.0f;   // l_part: fp32 weights, for LSE
-  float l_rnd = 0.0f;                        // bf16-rounded weights, for O
-  uint16_t* myV = sVt[wave];
-
-  for (int k0 = ks + wave * kSub; k0 < ke; k0 += kWaves * kSub) {
-    // K rows as A operand: block e2 = 2p+e, row R -> key 32p + (R/4)*8 + e*4 + R%4
-    u32x4 kf[4][DT];
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int p = blk >> 1, e = blk & 1;
-      const int key = k0 + 32 * p + (l16 >> 2) * 8 + e * 4 + (l16 & 3);
-#pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key < ke) w = load16(kbase + (int64_t)key * row_stride + t * 32 + grp * 8);
-        kf[blk][t] = w;
-      }
-    }
-    // V rows, 4-key x 8-dim blocks
-    u32x4 vr[VIT][4];
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int blkid = it * 64 + lane;
-      const int dc = blkid % KCH, kq = blkid / KCH;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + kq * 4 + r;
-        u32x4 w = {0u, 0u, 0u, 0u};
-        if (key < ke) w = load16(vbase + (int64_t)key * row_stride + dc * 8);
-        vr[it][r] = w;
-      }
-    }
-
-    // S^T blocks: lane (n, grp) item r of block 2p+e = key 32p + grp*8 + e*4 + r
-    f32x4 s[4];
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      s[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < DT; ++t)
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[blk][t]), qf[t], s[blk], 0, 0, 0);
-    }
-
-    // V^T into this wave's LDS tile
-#pragma unroll
-    for (int it = 0; it < VIT; ++it) {
-      const int blkid = it * 64 + lane;
-      const int dc = blkid % KCH, kq = blkid / KCH;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        u32x2 out;
-        if ((e & 1) == 0) {
-          out[0] = (vr[it][0][w] & 0xffffu) | (vr[it][1][w] << 16);
-          out[1] = (vr[it][2][w] & 0xffffu) | (vr[it][3][w] << 16);
-        } else {
-          out[0] = (vr[it][0][w] >> 16) | (vr[it][1][w] & 0xffff0000u);
-          out[1] = (vr[it][2][w] >> 16) | (vr[it][3][w] & 0xffff0000u);
-        }
-        const int row = dc * 8 + e;
-        *reinterpret_cast<u32x2*>(&myV[row * kSub + (((kq >> 1) ^ swz_d(row)) * 8) + (kq & 1) * 4]) = out;
-      }
-    }
-
-    // online softmax for query head l16 over this sub-tile's keys
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int p = blk >> 1, e = blk & 1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 32 * p + grp * 8 + e * 4 + r;
-        s[blk][r] = key < ke ? s[blk][r] : -INFINITY;
-        mx = fmaxf(mx, s[blk][r]);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mt = mx * c;
-    const bool need = mt > m_ref + kRescaleSlack;
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
-      const float m_new = need ? mt : m_ref;
-      const float alpha = need ? fast_exp2(m_ref - m_new) : 1.0f;
-      m_ref = m_new;
-      l_part *= alpha;
-      l_rnd *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) acc[d] *= alpha;
-    }
-    const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
-    float pv[4][4];
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[blk][r] = fast_exp2(fmaf(s[blk][r], c, -mu));
-        l_part += pv[blk][r];
-      }
-    bf16x8 pf[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float f8[8] = {pv[2 * p][0],     pv[2 * p][1],     pv[2 * p][2],     pv[2 * p][3],
-                           pv[2 * p + 1][0], pv[2 * p + 1][1], pv[2 * p + 1][2], pv[2 * p + 1][3]};
-      pf[p] = pack_bf16x8_sum(f8, &l_rnd);
-    }
-
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // O^T += V^T P^T: lane (dd row l16, grp) slot s = key 32p + grp*8 + s
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const int row = d * 16 + l16;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, load16(&myV[row * kSub + (((4 * p + grp) ^ swz_d(row)) * 8)]));
-        acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[p], acc[d], 0, 0, 0);
-      }
-
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  // ---- merge the four waves: sum over lane groups, then across waves in LDS
-  l_part += __shfl_xor(l_part, 16, 64);
-  l_part += __shfl_xor(l_part, 32, 64);
-  l_rnd += __shfl_xor(l_rnd, 16, 64);
-  l_rnd += __shfl_xor(l_rnd, 32, 64);
-  __syncthreads();                                     // V^T tiles are free again
-  float* s_o = reinterpret_cast<float*>(&sVt[0][0]);   // [kWaves][kGMax][D] fp32 (fits: 4*16*128*4 = 32 KB)
-  if (grp == 0) {
-    s_m[wave][l16] = m_ref;
-    s_l[wave][l16] = l_part;
-    s_lr[wave][l16] = l_rnd;
-  }
-#pragma unroll
-  for (int d = 0; d < DB; ++d)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) s_o[(wave * kGMax + l16) * D + d * 16 + grp * 4 + r] = acc[d][r];
-  __syncthreads();
-
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int n = idx / D, dd = idx % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][n]);
-    float Lsum = 0.0f, Lrnd = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float sc = s_m[w][n] == -INFINITY ? 0.0f : fast_exp2(s_m[w][n] - M);
-      Lsum += s_l[w][n] * sc;
-      Lrnd += s_lr[w][n] * sc;
-      O += s_o[(w * kGMax + n) * D + dd] * sc;
-    }
-    const int h = g * G + n;
-    const int64_t slot = ((int64_t)b * Hq + h) * max_splits + split;
-    part_o[slot * D + dd] = O / Lrnd;
-    if (dd == 0) part_lse[slot] = (M + fast_log2(Lsum)) * kLn2;
+// The sequence holding unit u: the largest b < B with cu[b] * Hkv <= u
+// (cu is non-decreasing and cu[0] = 0), found 64 entries at a time.
+__device__ __forceinline__ int sequence_of(const int32_t* __restrict__ cu, int B, int Hkv, int64_t u) {
+  const int lane = threadIdx.x & 63;
+  for (int c0 = 0;; c0 += 64) {
+    const int i = c0 + lane;
+    const bool le = i < B && (int64_t)cu[i] * Hkv <= u;
+    const int cnt = __builtin_popcountll(__builtin_amdgcn_ballot_w64(le));
+    if (cnt < 64 || c0 + 64 >= B) return c0 + cnt - 1;
   }
 }
 
 template <int D>
-__global__ __launch_bounds__(D) void decode_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_lse,
-                                                           const int32_t* __restrict__ cu,
-                                                           uint16_t* __restrict__ o, float* __restrict__ lse,
-                                                           int Hq, int max_splits, int chunk) {
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ cu, float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq,
+    int Hkv, int W, float c) {
+  constexpr int DT = D / 32;                  // MFMA k-steps of S^T (32 head-dim values each)
+  constexpr int DB = D / 16;                  // 16-wide head-dim blocks of O^T
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int RPL = 64 / CPR;               // rows per wave load
+  constexpr int VL = kTile / RPL;             // loads per tile and tensor
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[kTile * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[kTile * D];
+
+  const int w = blockIdx.x;
+  const int64_t K = (int64_t)cu[B] * Hkv;
+  int64_t u = part_bound(w, K, W);
+  const int64_t u_end = part_bound(w + 1, K, W);
+  if (u >= u_end) return;                              // no units for this wave
+  const int G = Hq / Hkv;
+
+  const int lane = threadIdx.x;
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;                           // 0..3
+  const uint32_t rstride = (uint32_t)Hkv * D * 2;     // bytes between cache rows
+  // lane l of load u takes row u*RPL + l/CPR, logical chunk l%CPR
+  const int row_l = lane / CPR;
+  const uint32_t ld_lane = (uint32_t)row_l * rstride + (lane % CPR) * 16;
+
+  // ---- lane-constant LDS byte offsets
+  // tile stores: row u*RPL + row_l, physical chunk (lane%CPR) ^ swz
+  // K read (A operand of S^T): row 16kb + l16, logical chunk 4s + grp (the
+  // swizzle depends on the row's low 4 bits only, so kb adds 16 rows)
+  int k_rd[DT];
+#pragma unroll
+  for (int st = 0; st < DT; ++st) k_rd[st] = l16 * (2 * D) + (((4 * st + grp) ^ swz_k<CPR>(l16)) * 16);
+  // V^T read (ds_read_b64_tr_b16): lane r of group grp points at key row
+  // 4grp + r/4 (+16 for the second read) and head-dim 16db + 4(r%4).
+  const int trow = 4 * grp + (l16 >> 2);
+  int v_rd[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int chunk16 = 2 * db + ((l16 & 3) >> 1);
+    v_rd[db] = trow * (2 * D) + ((chunk16 ^ swz_v<CPR>(trow)) * 16) + (l16 & 1) * 8;
+  }
+  char* const sKb = reinterpret_cast<char*>(&sK[0]);
+  char* const sVb = reinterpret_cast<char*>(&sV[0]);
+
+  int b = sequence_of(cu, B, Hkv, u);
+  while (u < u_end) {
+    const int start = cu[b];
+    const int L = cu[b + 1] - start;
+    const int64_t ub = (int64_t)start * Hkv;           // first unit of sequence b
+    if (u >= ub + (int64_t)L * Hkv) {                  // past sequence b (or it is empty)
+      ++b;
+      continue;
+    }
+    // ---- the piece: keys [k0, k0 + n) of (sequence b, kv head g)
+    const int g = (int)((u - ub) / L);
+    const int k0 = (int)(u - ub - (int64_t)g * L);
+    const int64_t piece_end = min(u_end, ub + (int64_t)(g + 1) * L);
+    const int n = (int)(piece_end - u);
+
+    // buffer views over the piece's rows of kv head g; rows >= n read 0
+    const int64_t row0 = ((int64_t)(start + k0) * Hkv + g) * D;
+    const uint32_t nbytes = (uint32_t)((n - 1) * Hkv + 1) * D * 2;
+    const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kc + row0, nbytes);
+    const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vc + row0, nbytes);
+    auto load_tile = [&](KvTile<D>& t, const int tile) {
+      const uint32_t base = (uint32_t)tile * kTile * rstride + ld_lane;
+#pragma unroll
+      for (int i = 0; i < VL; ++i) t.k[i] = buffer_load16(k_rsrc, base + i * RPL * rstride);
+#pragma unroll
+      for (int i = 0; i < VL; ++i) t.v[i] = buffer_load16(v_rsrc, base + i * RPL * rstride);
+      // issue these loads before any of the following compute (the scheduler
+      // would otherwise hoist the previous tile's first wait above them)
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Q^T as B operand: column j = query head g*G + j (zero for j >= G)
+    bf16x8 qf[DT];
+    {
+      const bool valid = l16 < G;
+      const uint16_t* src = q + ((int64_t)b * Hq + g * G + (valid ? l16 : 0)) * D + grp * 8;
+#pragma unroll
+      for (int st = 0; st < DT; ++st) {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (valid) x = load16(src + st * 32);
+        qf[st] = __builtin_bit_cast(bf16x8, x);
+      }
+    }
+
+    f32x4 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY;   // reference max of head l16 (base-2 domain), same in its 4 lanes
+    float l_part = 0.0f;       // fp32 weights of this lane's keys (for LSE)
+    float l_rnd = 0.0f;        // bf16-rounded weights of this lane's keys (for O)
+
+    auto compute_tile = [&](const KvTile<D>& t, const int tile) {
+      // K and V rows -> LDS (the previous tile's reads were issued before;
+      // LDS accesses of one wave complete in order)
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int row = i * RPL + row_l;
+        store16(sKb + row * (2 * D) + (((lane % CPR) ^ swz_k<CPR>(row)) * 16), t.k[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < VL; ++i) {
+        const int row = i * RPL + row_l;
+        store16(sVb + row * (2 * D) + (((lane % CPR) ^ swz_v<CPR>(row)) * 16), t.v[i]);
+      }
+      // S^T: lane (head l16, group grp) item r of block kb = key 16kb + 4grp + r
+      f32x4 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < DT; ++st) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, load16(sKb + kb * 16 * (2 * D) + k_rd[st]));
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[st], s[kb], 0, 0, 0);
+        }
+      }
+      // mask keys past the piece's end, then the online softmax of head l16
+      const int thr = n - 1 - (tile * kTile + 4 * grp);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[kb][r] = 16 * kb + r <= thr ? s[kb][r] : -INFINITY;
+          mx = fmaxf(mx, s[kb][r]);
+        }
+      mx = max_xor16(mx);
+      mx = max_xor32(mx);
+      const float mt = mx * c;
+      const bool need = mt > m_ref + kRescaleSlack;
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(need) != 0, 0)) {
+        const float m_new = need ? mt : m_ref;
+        const float alpha = need ? fast_exp2(m_ref - m_new) : 1.0f;   // 0 when m_ref was -inf
+        m_ref = m_new;
+        l_part *= alpha;
+        l_rnd *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+      }
+      const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
+      float p[8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[4 * kb + r] = fast_exp2(fmaf(s[kb][r], c, -mu));
+          l_part += p[4 * kb + r];
+        }
+      const bf16x8 pf = pack_bf16x8_sum(p, &l_rnd);
+      // O^T += V^T P^T: items 0..3 = keys 4grp.., items 4..7 = keys 16+4grp..
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x2 lo = lds_read_tr16(sVb + v_rd[db]);
+        const u32x2 hi = lds_read_tr16(sVb + v_rd[db] + 16 * (2 * D));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, acc[db], 0, 0, 0);
+      }
+    };
+
+    // two-stage register pipeline over the piece's tiles.  Tiles past the end
+    // read 0 (no memory traffic) and are fully masked, so they add nothing;
+    // the loads and computes are unconditional so that the only waits are for
+    // the tile about to be used (a load issued on one path only would make the
+    // compiler wait for every load at the join).
+    const int ntiles = (n + kTile - 1) / kTile;
+    KvTile<D> ta, tb;
+    load_tile(ta, 0);
+    for (int t = 0; t < ntiles; t += 2) {
+      load_tile(tb, t + 1);
+      compute_tile(ta, t);
+      load_tile(ta, t + 2);
+      compute_tile(tb, t + 1);
+    }
+
+    // partial result of the piece: O_s = O / l_rnd, LSE_s = (m + log2 l) ln 2
+    l_part += __shfl_xor(l_part, 16, 64);
+    l_part += __shfl_xor(l_part, 32, 64);
+    l_rnd += __shfl_xor(l_rnd, 16, 64);
+    l_rnd += __shfl_xor(l_rnd, 32, 64);
+    if (l16 < G) {
+      const int64_t slot = piece_slot(k0 == 0, w, W, b, Hkv, g) * G + l16;
+      const float inv = 1.0f / l_rnd;
+      float* dst = part_o + slot * D + 4 * grp;
+      // lane (head l16, group grp) item r of block db holds head-dim 16db + 4grp + r
+#pragma unroll
+      for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = acc[db] * inv;
+      if (grp == 0) part_lse[slot] = (m_ref + fast_log2(l_part)) * kLn2;
+    }
+    u = piece_end;
+  }
+}
+
+// One workgroup per (sequence, query head): merges the pieces of its (sequence,
+// kv head): the first piece, in slot W + b*Hkv + g, and one continuation per
+// non-empty wave that starts inside the range, in that wave's slot.  PL lanes
+// of pieces (kCombineThreads / D) each fold every PL-th piece, kBatch pieces
+// at a time with all their loads issued first; the lanes are then merged
+// through LDS.
+constexpr int kCombineThreads = 256;
+constexpr int kBatch = 16;
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, const int32_t* __restrict__ cu,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int W) {
+  constexpr int PL = kCombineThreads / D;
+  __shared__ float s_m[PL], s_w[PL];
+  __shared__ float s_acc[PL][D];
   const int bh = blockIdx.x;
-  const int b = bh / Hq;
-  const int L = cu[b + 1] - cu[b];
-  const int ns = min((L + chunk - 1) / chunk, max_splits);   // lengths above the bound are a caller error
-  const int dd = threadIdx.x;
-  const float* pl = part_lse + (int64_t)bh * max_splits;
-  const float* po = part_o + (int64_t)bh * max_splits * D;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pl[s]);
-  float wsum = 0.0f, acc = 0.0f;
-  if (ns > 0) {
-    for (int s = 0; s < ns; ++s) {
-      const float w = fast_exp2((pl[s] - M) * kLog2e);
-      wsum += w;
-      acc = fmaf(w, po[(int64_t)s * D + dd], acc);
+  const int b = bh / Hq, h = bh % Hq;
+  const int G = Hq / Hkv;
+  const int g = h / G, j = h % G;
+  const int pl = threadIdx.x / D, dd = threadIdx.x % D;
+  const int start = cu[b];
+  const int L = cu[b + 1] - start;
+  if (L == 0 || W == 0) {                              // no keys: O = 0, LSE = -inf
+    if (pl == 0) {
+      o[(int64_t)bh * D + dd] = 0;
+      if (dd == 0) lse[bh] = -INFINITY;
+    }
+    return;
+  }
+  const int64_t K = (int64_t)cu[B] * Hkv;
+  const int64_t U = (int64_t)start * Hkv + (int64_t)g * L;
+  const int lo = wave_of(U, K, W), hi = wave_of(U + L - 1, K, W);
+  const int npieces = 1 + (hi - lo);
+  // a wave has no units only when there are fewer units than waves
+  const bool may_be_empty = K < W;
+  // fold with a running max over the (natural-log) piece LSEs
+  float M = -INFINITY, wsum = 0.0f, acc = 0.0f;
+  for (int base = pl; base < npieces; base += PL * kBatch) {
+    float ls[kBatch], ov[kBatch];
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const int i = base + t * PL;
+      const int wv = lo + i;
+      // wave wv >= lo+1 holds a piece of this range unless it has no units
+      const bool ok = i < npieces &&
+                      (i == 0 || !may_be_empty || part_bound(wv, K, W) < part_bound(wv + 1, K, W));
+      const int64_t slot = piece_slot(i == 0, wv, W, b, Hkv, g) * G + j;
+      ls[t] = ok ? part_lse[slot] : -INFINITY;
+      ov[t] = ok ? part_o[slot * D + dd] : 0.0f;
+    }
+    float bm = M;
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) bm = fmaxf(bm, ls[t]);
+    if (bm == -INFINITY) continue;
+    const float sc = M == -INFINITY ? 0.0f : fast_exp2((M - bm) * kLog2e);
+    acc *= sc;
+    wsum *= sc;
+    M = bm;
+#pragma unroll
+    for (int t = 0; t < kBatch; ++t) {
+      const float wt = ls[t] == -INFINITY ? 0.0f : fast_exp2((ls[t] - M) * kLog2e);
+      wsum += wt;
+      acc = fmaf(wt, ov[t], acc);
     }
   }
-  const float out = ns > 0 ? acc / wsum : 0.0f;
-  o[(int64_t)bh * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)out);
-  if (dd == 0) lse[bh] = ns > 0 ? M + fast_log2(wsum) * kLn2 : -INFINITY;
+  if (dd == 0) {
+    s_m[pl] = M;
+    s_w[pl] = wsum;
+  }
+  s_acc[pl][dd] = acc;
+  __syncthreads();
+  if (pl != 0) return;
+  float Mt = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) Mt = fmaxf(Mt, s_m[i]);
+  float wt = 0.0f, out = 0.0f;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const float sc = s_m[i] == -INFINITY ? 0.0f : fast_exp2((s_m[i] - Mt) * kLog2e);
+    wt += s_w[i] * sc;
+    out = fmaf(s_acc[i][dd], sc, out);
+  }
+  o[(int64_t)bh * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(out / wt));
+  if (dd == 0) lse[bh] = Mt + fast_log2(wt) * kLn2;
 }
 
 template <int D>
 hipError_t launch(const DecodeArgs& a) {
-  const int64_t nblk = (int64_t)a.B * a.Hkv * a.max_splits;
-  if (nblk > 0) {
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)nblk), dim3(kThreads), 0, a.stream,
+  if (a.waves > 0) {
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)a.waves), dim3(64), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.cu,
-                       a.part_o, a.part_lse, a.Hq, a.Hkv, a.max_splits, a.chunk, a.scale * kLog2e);
-    hipError_t e = hipGetLastError();
+                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, a.waves, a.scale * kLog2e);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(D), 0, a.stream,
-                     a.part_o, a.part_lse, a.cu, (uint16_t*)a.o, a.lse, a.Hq, a.max_splits, a.chunk);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(kCombineThreads), 0,
+                     a.stream, a.part_o, a.part_lse, a.cu, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.waves);
   return hipGetLastError();
 }
 
@@ -296,6 +392,5 @@ hipError_t launch(const DecodeArgs& a) {
 hipError_t launch_decode_bf16(const DecodeArgs& a) { return a.d == 64 ? launch<64>(a) : launch<128>(a); }
 
 int decode_max_group() { return kGMax; }
-int decode_chunk_granule() { return kWaves * kSub; }
 
 }  // namespace fa

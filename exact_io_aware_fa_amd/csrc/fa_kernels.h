@@ -26,10 +26,10 @@ struct DecodeArgs {
   const int32_t* cu;
   void* o;
   float* lse;
-  float* part_o;      // [B, Hq, max_splits, d] fp32
-  float* part_lse;    // [B, Hq, max_splits] fp32
+  float* part_o;      // [waves + B*Hkv, Hq/Hkv, d] fp32 partial outputs
+  float* part_lse;    // [waves + B*Hkv, Hq/Hkv] fp32 partial logsumexps
   int B, Hq, Hkv, d;
-  int max_splits, chunk;
+  int waves;          // split-kernel waves (0: no keys to attend)
   float scale;
   hipStream_t stream;
 };
@@ -39,6 +39,5 @@ hipError_t launch_prefill_f32(const PrefillArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
 
 int decode_max_group();       // largest Hq/Hkv the decode kernel handles
-int decode_chunk_granule();   // split sizes are multiples of this many keys
 
 }  // namespace fa

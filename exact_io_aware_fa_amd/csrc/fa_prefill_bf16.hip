@@ -116,9 +116,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
   const __amdgpu_buffer_rsrc_t q_rsrc =
       make_rsrc(q + ((int64_t)b * N * Hq + h) * D, (uint32_t)((N - 1) * Hq + 1) * D * 2);
+  // K/V: one view per tile (built in issue_k / issue_v), starting at the
+  // tile's first row and ending at the slice's last row, so that rows past
+  // Nk read as 0.  (The scalar offset of a buffer access is not range
+  // checked, so the tile offset goes into the base, not into soffset.)
+  const uint16_t* k_slice = k + ((int64_t)b * Nk * Hkv + g) * D;
+  const uint16_t* v_slice = v + ((int64_t)b * Nk * Hkv + g) * D;
   const uint32_t kv_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * Hkv + 1) * D * 2 : 0u;
-  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(k + ((int64_t)b * Nk * Hkv + g) * D, kv_bytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(v + ((int64_t)b * Nk * Hkv + g) * D, kv_bytes);
 
   // ---- Q tile -> registers (B operand of S^T = K Q^T); rows past N read 0
   bf16x8 qf[DSTEPS];
@@ -157,17 +161,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     k_voff[i] = (uint32_t)row * kv_row_bytes + (uint32_t)((pc ^ swz_k<CPR>(row)) * 16);
     v_voff[i] = (uint32_t)row * kv_row_bytes + (uint32_t)((pc ^ swz_v<CPR>(row)) * 16);
   }
+  // tile j begins j*kBC rows (tile_off bytes) into the slice; j < n_kv, so
+  // it begins before the slice's end
   auto issue_k = [&](int j, int st) {
     const uint32_t tile_off = (uint32_t)(j * kBC) * kv_row_bytes;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(k_slice + (int64_t)j * kBC * Hkv * D, kv_bytes - tile_off);
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
-      buffer_load16_to_lds(k_rsrc, k_voff[i], tile_off, (lds_void*)&sK[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
+      buffer_load16_to_lds(r, k_voff[i], 0, (lds_void*)&sK[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
   };
   auto issue_v = [&](int j, int st) {
     const uint32_t tile_off = (uint32_t)(j * kBC) * kv_row_bytes;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(v_slice + (int64_t)j * kBC * Hkv * D, kv_bytes - tile_off);
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
-      buffer_load16_to_lds(v_rsrc, v_voff[i], tile_off, (lds_void*)&sV[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
+      buffer_load16_to_lds(r, v_voff[i], 0, (lds_void*)&sV[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
   };
 
   // ---- lane-constant LDS offsets (bytes) for the MFMA operand reads

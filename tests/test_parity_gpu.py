@@ -215,6 +215,31 @@ def test_masked_keys_have_no_effect_bitwise(dtype, d):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rows_past_the_end_are_never_read(d, causal, dtype):
+    """K and V are the first Nk rows of a larger allocation whose remaining
+    rows hold NaN (Nk is not a multiple of any tile size, so the last tile is
+    ragged).  A kernel that read any row past Nk, even only to multiply it by a
+    zero weight, would put NaN into O; the output must match the oracle."""
+    B, Hq, Hkv, N, Nk = 1, 4, 2, 150, 333
+    q, k, v = inputs.prefill_inputs(B, N, Nk, Hq, Hkv, d, dtype, seed=21)
+    pad = 200
+    kbig = torch.full((B, Nk + pad, Hkv, d), float("nan"), dtype=dtype, device="cuda")
+    vbig = torch.full((B, Nk + pad, Hkv, d), float("nan"), dtype=dtype, device="cuda")
+    kbig[:, :Nk] = k.cuda()
+    vbig[:, :Nk] = v.cuda()
+    kd, vd = kbig[:, :Nk], vbig[:, :Nk]
+    assert kd.is_contiguous() and vd.is_contiguous()
+    o, lse = binding.fwd(q.cuda(), kd, vd, causal, inputs.fp32_scale(d))
+    torch.cuda.synchronize()
+    ro, rlse = oracle.attention(q, k, v, causal, inputs.fp32_scale(d))
+    tol_o, tol_l = TOL[dtype]
+    assert_close(o.cpu(), ro, tol_o, "O")
+    assert_close(lse.cpu(), rlse, tol_l, "LSE")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_first_causal_row_returns_v0_bitwise(dtype):
     q, k, v = inputs.prefill_inputs(2, 129, 129, 8, 2, 128, dtype, seed=4)
     o, lse = gpu_fwd(q, k, v, True, inputs.fp32_scale(128))
@@ -290,6 +315,24 @@ def test_decode_other_sequences_have_no_effect_bitwise():
     for b in (0, 2):
         assert torch.equal(o1[b], o2[b]) and torch.equal(l1[b], l2[b])
     assert not torch.equal(o1[1], o2[1])
+
+
+def test_decode_cache_rows_past_the_end_are_never_read():
+    """The packed caches are the first sum(L) rows of larger allocations whose
+    remaining rows hold NaN; reading any of them would put NaN into O."""
+    lens = [37, 1000, 2049, 333]
+    Hq, Hkv, d = 16, 2, 128
+    q, kc, vc, cu = inputs.decode_inputs(lens, Hq, Hkv, d, torch.bfloat16, seed=13)
+    total, pad = int(cu[-1]), 300
+    kbig = torch.full((total + pad, Hkv, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vbig = torch.full((total + pad, Hkv, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    kbig[:total] = kc.cuda()
+    vbig[:total] = vc.cuda()
+    o, lse = binding.decode(q.cuda(), kbig[:total], vbig[:total], cu.cuda(), max(lens), inputs.fp32_scale(d))
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(q, kc, vc, cu, inputs.fp32_scale(d))
+    assert_close(o.cpu(), ro, 1e-2, "O")
+    assert_close(lse.cpu(), rl, 1e-3, "LSE")
 
 
 def test_decode_visible_count_is_exact():

@@ -17,6 +17,8 @@ algorithmic bytes (K and V cache, q, o, lse and cu_seqlens, each once).
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --pmc-pass      # one launch of each kernel plus a copy of known
                                     # size, for rocprofv3 counter collection
+    python bench.py --traffic-summary FETCH.csv WRITE.csv
+                                    # counters of two such passes -> profiles/traffic.json
 """
 import argparse
 import hashlib
@@ -33,9 +35,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 METRIC = ("attention fwd TFLOP/s & % bf16 MFMA peak (prefill); "
           "GB/s & % HBM peak (decode)")
-KERNEL_SOURCES = ["exact_io_aware_fa_amd/csrc/fa_prefill_bf16.hip",
-                  "exact_io_aware_fa_amd/csrc/fa_decode.hip",
-                  "exact_io_aware_fa_amd/csrc/fa_common.h"]
+_CSRC = "exact_io_aware_fa_amd/csrc/"
+# sources whose change invalidates a kernel's measured traffic
+TRAFFIC_SOURCES = {
+    "prefill": [_CSRC + "fa_prefill_bf16.hip", _CSRC + "fa_common.h"],
+    "decode": [_CSRC + "fa_decode.hip", _CSRC + "fa_common.h", _CSRC + "fa_api.cpp"],
+}
+# kernel-name fragments of each part (decode = split + combine)
+TRAFFIC_KERNELS = {"prefill": ["prefill_bf16_kernel"], "decode": ["decode_split_kernel", "decode_combine_kernel"]}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PMC_COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 
@@ -45,17 +52,61 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, sources):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel sources changed since it was taken."""
+def measured_traffic(part):
+    """HBM bytes per launch of `part` from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)[kernel_key]
+            rec = json.load(f)[part]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("sources") != {p: source_digest(p) for p in sources}:
+    if rec.get("sources") != {p: source_digest(p) for p in TRAFFIC_SOURCES[part]}:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_per_dispatch(csv_path, counter):
+    """{dispatch id: (kernel name, value summed over the counter's instances)}"""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            name, val = out.get(r["Dispatch_Id"], (r["Kernel_Name"], 0.0))
+            out[r["Dispatch_Id"]] = (name, val + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """HBM traffic per launch from two rocprofv3 counter passes over
+    `bench.py --pmc-pass` (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch).
+    Each counter is scaled by what it reads for the pass's 1 GiB device copy
+    (the largest copy dispatch), then summed over the kernels of one launch.
+    Writes profiles/traffic.json (with digests of the kernel sources) and
+    prints the figures."""
+    result = {}
+    factors = {}
+    per_part = {part: {} for part in TRAFFIC_KERNELS}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        disp = _counter_per_dispatch(path, counter)
+        copies = [v for n, v in disp.values() if "copyBuffer" in n]
+        factor = PMC_COPY_BYTES / (max(copies) * 1024.0)
+        factors[counter] = factor
+        for part, frags in TRAFFIC_KERNELS.items():
+            per_part[part][counter] = sum(v * 1024.0 * factor for n, v in disp.values()
+                                          if any(fr in n for fr in frags))
+    for part, c in per_part.items():
+        result[part] = {"fetch_bytes_per_launch": round(c["FETCH_SIZE"]),
+                        "write_bytes_per_launch": round(c["WRITE_SIZE"]),
+                        "hbm_bytes_per_launch": round(c["FETCH_SIZE"] + c["WRITE_SIZE"]),
+                        "sources": {p: source_digest(p) for p in TRAFFIC_SOURCES[part]}}
+    result["calibration"] = {"copy_bytes": PMC_COPY_BYTES, "fetch_factor": round(factors["FETCH_SIZE"], 4),
+                             "write_factor": round(factors["WRITE_SIZE"], 4)}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(result, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(result, indent=1, sort_keys=True))
 
 
 def prefill_flops(cfg):
@@ -93,7 +144,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter passes into profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU; this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -168,8 +224,8 @@ def main():
     dbytes = decode_bytes(dcfg, total_len)
     gbs = dbytes / (dec_avg * 1e-3) / 1e9
 
-    pre_traffic = measured_traffic("prefill_bf16_kernel", KERNEL_SOURCES[::2])
-    dec_traffic = measured_traffic("decode", KERNEL_SOURCES[1:])
+    pre_traffic = measured_traffic("prefill")
+    dec_traffic = measured_traffic("decode")
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),

@@ -112,11 +112,12 @@ __device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, u
 // buffer->LDS copies) are outstanding: s_waitcnt vmcnt(N), 0 <= N < 16.
 template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
+  // gfx9 s_waitcnt: vmcnt is bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
+  static_assert(N >= 0 && N < 64, "vmcnt field");
   // the fence keeps the scheduler from hoisting the wait above register-only
   // work that precedes it (it would then wait for the copies too early)
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
 }
 __device__ __forceinline__ void wait_vmem_all() { wait_vmem_le<0>(); }
 

@@ -58,6 +58,14 @@ constexpr int kBC = 64;             // keys per KV tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr float kRescaleSlack = 8.0f;
+// K/V tiles are copied kPD tiles ahead of their use, through rings of kNS
+// LDS stages per tensor (the copy of K_{j+kPD} and V_{j+kPD-1} is issued while
+// tile j is computed).
+#ifndef PREFILL_PD
+#define PREFILL_PD 3
+#endif
+constexpr int kPD = PREFILL_PD;
+constexpr int kNS = kPD + 1;
 
 // Accumulator row R of a 32x32 MFMA lives in lane half (R>>2)&1, item
 // (R>>3)*4 + (R&3).  Feeding K row pi32(R) as A-operand row R puts key h*16+r
@@ -86,8 +94,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   constexpr int DMA_PER_WAVE = TILE_ELEMS * 2 / 1024 / (kWaves / 2);   // issued by group 0
   static_assert(DMA_PER_WAVE >= 1, "each issuing wave issues at least one DMA per tensor");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sK[2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(1024))) uint16_t sV[2][TILE_ELEMS];
+  // One LDS variable per stage: the compiler keeps apart the accesses it can
+  // attribute to different variables, so a copy in flight into one stage does
+  // not make it wait before reads of another (the stage loops below are
+  // unrolled so that every stage is named statically).
+  static_assert(kNS <= 4, "at most four stages per tensor");
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK2[kNS > 2 ? TILE_ELEMS : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK3[kNS > 3 ? TILE_ELEMS : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV2[kNS > 2 ? TILE_ELEMS : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV3[kNS > 3 ? TILE_ELEMS : 8];
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   if (logical >= n_work) return;
@@ -161,21 +180,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     k_voff[i] = (uint32_t)row * kv_row_bytes + (uint32_t)((pc ^ swz_k<CPR>(row)) * 16);
     v_voff[i] = (uint32_t)row * kv_row_bytes + (uint32_t)((pc ^ swz_v<CPR>(row)) * 16);
   }
-  // tile j begins j*kBC rows (tile_off bytes) into the slice; j < n_kv, so
-  // it begins before the slice's end
-  auto issue_k = [&](int j, int st) {
-    const uint32_t tile_off = (uint32_t)(j * kBC) * kv_row_bytes;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(k_slice + (int64_t)j * kBC * Hkv * D, kv_bytes - tile_off);
-#pragma unroll
-    for (int i = 0; i < DMA_PER_WAVE; ++i)
-      buffer_load16_to_lds(r, k_voff[i], 0, (lds_void*)&sK[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
+  // Tile j begins j*kBC rows (tile_off bytes) into the slice.  Every call
+  // issues the same number of copies: for a tile that does not exist (j >=
+  // n_kv) the view is empty, so the copy writes zeros into a free stage and
+  // reads nothing; the waits below count copies.
+  auto tile_view = [&](const uint16_t* slice, const int j) {
+    const bool real = j < n_kv;
+    const uint32_t tile_off = real ? (uint32_t)(j * kBC) * kv_row_bytes : 0u;
+    return make_rsrc(slice + (real ? (int64_t)j * kBC * Hkv * D : 0), real ? kv_bytes - tile_off : 0u);
   };
-  auto issue_v = [&](int j, int st) {
-    const uint32_t tile_off = (uint32_t)(j * kBC) * kv_row_bytes;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(v_slice + (int64_t)j * kBC * Hkv * D, kv_bytes - tile_off);
+  auto issue = [&](const uint16_t* slice, const int j, const uint32_t* voff, char* stage) {
+    const __amdgpu_buffer_rsrc_t r = tile_view(slice, j);
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
-      buffer_load16_to_lds(r, v_voff[i], 0, (lds_void*)&sV[st][(dma_wave * DMA_PER_WAVE + i) * 512]);
+      buffer_load16_to_lds(r, voff[i], 0, (lds_void*)(stage + (dma_wave * DMA_PER_WAVE + i) * 1024));
+  };
+  // stage st of each ring (a constant st names one variable)
+  auto kS = [&](const int st) -> char* {
+    return reinterpret_cast<char*>(st == 0 ? sK0 : st == 1 ? sK1 : st == 2 ? sK2 : sK3);
+  };
+  auto vS = [&](const int st) -> char* {
+    return reinterpret_cast<char*>(st == 0 ? sV0 : st == 1 ? sV1 : st == 2 ? sV2 : sV3);
   };
 
   // ---- lane-constant LDS offsets (bytes) for the MFMA operand reads
@@ -212,9 +237,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   f32x16 s[2];               // scores of the current tile (two 32-key blocks)
   bf16x8 pf[2][2];           // weights of the current tile, B operands of P.V
 
-  // S^T = K Q^T for the tile in K stage `kst_i`
-  auto stage_s = [&](const int kst_i) {
-    const char* kst = reinterpret_cast<const char*>(&sK[kst_i][0]);
+  // S^T = K Q^T for the K tile at `kst`
+  auto stage_s = [&](const char* kst) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -229,15 +253,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     }
   };
 
-  // O^T = alpha*O^T + V^T P^T for the tile in V stage `vst_i`
-  auto stage_pv = [&](const int vst_i) {
+  // O^T = alpha*O^T + V^T P^T for the V tile at `vst`
+  auto stage_pv = [&](const char* vst) {
     if (__builtin_expect(rescale, 0)) {
 #pragma unroll
       for (int d = 0; d < DBLK; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[d][r] *= alpha;
     }
-    const char* vst = reinterpret_cast<const char*>(&sV[vst_i][0]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -253,11 +276,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
         }
   };
 
-  // online softmax of the tile of keys j0..j0+63 -> pf, branch-free.  MASKED:
-  // some key of the tile is invisible to some row of this wave.
-  auto stage_softmax = [&](const int j0, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if (MASKED) {
+  // online softmax of the tile of keys j0..j0+63 -> pf.  `masked`
+  // (wave-uniform): some key of the tile is invisible to some row of this wave.
+  auto stage_softmax = [&](const int j0, const bool masked) {
+    if (__builtin_expect(masked, 0)) {
       // last visible key of this lane's row; item r of block kb holds key
       // j0 + kb*32 + hh*16 + r
       const int lim = CAUSAL ? min(Nk - 1, qbase + li + offs) : Nk - 1;
@@ -295,50 +317,92 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
       pf[kb][1] = pack_bf16x8_sum(&p[8], &l_rnd);
     }
   };
-  const auto kClean = std::integral_constant<bool, false>();
-  const auto kMasked = std::integral_constant<bool, true>();
+
+  // The MFMA block of tile j: P.V of tile j-1, S of tile j, and (group 0)
+  // the copies of K_{j+kPD} and V_{j+kPD-1}.  The read and copy stages are
+  // distinct; passing them as restrict pointers of one inlined call lets the
+  // compiler see that, so it does not wait for the copies in flight before
+  // the reads (the waits that order copies and reads are the explicit ones
+  // below, before the workgroup barriers).
+  auto mblock = [&](const int j, const char* __restrict__ kread, const char* __restrict__ vread,
+                    char* __restrict__ kdst, char* __restrict__ vdst, auto copy_tag) __attribute__((always_inline)) {
+    if (j >= 1) stage_pv(vread);
+    stage_s(kread);
+    if (decltype(copy_tag)::value) {
+      issue(k_slice, j + kPD, k_voff, kdst);
+      issue(v_slice, j + kPD - 1, v_voff, vdst);
+    }
+  };
+  const auto kCopy = std::integral_constant<bool, true>();
+  const auto kNoCopy = std::integral_constant<bool, false>();
+  constexpr int kCopiesPerBlock = 2 * DMA_PER_WAVE;
 
   // ---- ping-pong schedule.  Group g runs the MFMA block M_j = [P.V of tile
   // j-1, S of tile j] in phase 2j+g and the softmax V_j in phase 2j+1+g;
-  // both groups execute 2*n_kv + 2 barriers.  Group 0 issues the DMA of
-  // K_{j+1} and V_j at the end of M_j (into the stages tile j-1 used) and
-  // waits for it at the end of phase 2j+1; both groups read them from phase
-  // 2j+2 on.
+  // both groups execute 2*n_kv + 2 barriers.  Tile j lives in stage j % kNS
+  // of each ring.  Group 0 copies K_0..K_{kPD-1} and V_0..V_{kPD-2} before
+  // phase 0 and K_{j+kPD}, V_{j+kPD-1} at the end of M_j; at the end of phase
+  // 2j+1 it waits until the copies of K_{j+1} and V_j (issued kPD-1 blocks
+  // earlier) have landed, and the barrier publishes them to both groups.  A
+  // stage is overwritten only after both groups have finished reading its
+  // previous tile (K_{j-1}, V_{j-2}: read by the end of phase 2j-1).
   const int group = wave >= kWaves / 2 ? 1 : 0;
+  // Rounds of kNS tiles, unrolled so that every stage is named statically.
+  // The check after each tile leaves the loop (it never skips ahead to the
+  // next round), so at the top of a round, as far as the compiler can tell,
+  // the same copies are in flight as at the end of the previous one.
+  auto run_group = [&](auto copy_tag) __attribute__((always_inline)) {
+    constexpr bool COPY = decltype(copy_tag)::value;
+    auto step = [&](const int j, const int st) __attribute__((always_inline)) {   // j % kNS == st
+      mblock(j, kS(st), vS((st + kNS - 1) % kNS), kS((st + kPD) % kNS), vS((st + kPD - 1) % kNS),
+             copy_tag);                               // phase 2j+g
+      barrier_no_fence();
+      stage_softmax(j * kBC, j >= n_clean);           // phase 2j+1+g
+      if (COPY) wait_vmem_le<(kPD - 1) * kCopiesPerBlock>();
+      barrier_no_fence();
+    };
+    // one round from tile j0 (< n_kv); false once the last tile is done
+    auto round = [&](const int j0) __attribute__((always_inline)) -> bool {
+      step(j0, 0);
+      if (j0 + 1 >= n_kv) return false;
+      step(j0 + 1, 1);
+      if (j0 + 2 >= n_kv) return false;
+      if constexpr (kNS > 2) {
+        step(j0 + 2, 2);
+        if (j0 + 3 >= n_kv) return false;
+      }
+      if constexpr (kNS > 3) {
+        step(j0 + 3, 3);
+        if (j0 + 4 >= n_kv) return false;
+      }
+      return true;
+    };
+    for (int j0 = 0; round(j0); j0 += kNS) {
+    }
+  };
   if (n_kv > 0) {
     if (group == 0) {
-      issue_k(0, 0);
-      wait_vmem_all();
+#pragma unroll
+      for (int t = 0; t < kPD; ++t) issue(k_slice, t, k_voff, kS(t));
+#pragma unroll
+      for (int t = 0; t < kPD - 1; ++t) issue(v_slice, t, v_voff, vS(t));
     }
+    // both groups: the Q registers (and group 0's first copies) have landed.
+    // (Waiting in one group only would leave the loads pending, as far as the
+    // compiler can tell, where the groups' paths join, and it would then wait
+    // for them, and for every copy issued after them, inside the loops.)
+    wait_vmem_all();
     barrier_no_fence();
     if (group == 0) {
-      auto step = [&](const int j, auto masked_tag) {
-        if (j >= 1) stage_pv((j - 1) & 1);          // phase 2j: M_j
-        stage_s(j & 1);
-        if (j + 1 < n_kv) issue_k(j + 1, (j + 1) & 1);
-        issue_v(j, j & 1);
-        barrier_no_fence();
-        stage_softmax(j * kBC, masked_tag);          // phase 2j+1: V_j
-        wait_vmem_all();
-        barrier_no_fence();
-      };
-      for (int j = 0; j < n_clean; ++j) step(j, kClean);
-      for (int j = n_clean; j < n_kv; ++j) step(j, kMasked);
-      stage_pv((n_kv - 1) & 1);                     // phase 2n: M_n
+      run_group(kCopy);
+      wait_vmem_all();                              // no copy may land after the workgroup ends
+      stage_pv(vS((n_kv - 1) % kNS));               // phase 2n: M_n
       barrier_no_fence();
       barrier_no_fence();                           // phase 2n+1: idle
     } else {
       barrier_no_fence();                           // phase 0: idle
-      auto step = [&](const int j, auto masked_tag) {
-        if (j >= 1) stage_pv((j - 1) & 1);          // phase 2j+1: M_j
-        stage_s(j & 1);
-        barrier_no_fence();
-        stage_softmax(j * kBC, masked_tag);          // phase 2j+2: V_j
-        barrier_no_fence();
-      };
-      for (int j = 0; j < n_clean; ++j) step(j, kClean);
-      for (int j = n_clean; j < n_kv; ++j) step(j, kMasked);
-      stage_pv((n_kv - 1) & 1);                     // phase 2n+1: M_n
+      run_group(kNoCopy);
+      stage_pv(vS((n_kv - 1) % kNS));               // phase 2n+1: M_n
       barrier_no_fence();
     }
   }

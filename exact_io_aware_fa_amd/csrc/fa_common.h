@@ -62,6 +62,7 @@ __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cas
 __device__ __forceinline__ void store16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float wave_xor16(float x) { return __shfl_xor(x, 16, 64); }
 
 // max(x[l], x[l ^ 32]) without touching LDS: v_permlane32_swap_b32 a, b swaps
 // lanes 32..63 of a with lanes 0..31 of b, so with a = b = x, a and b hold the
@@ -69,18 +70,23 @@ __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 
 // ds_bpermute, an LDS instruction, and the compiler then waits for every
 // outstanding buffer->LDS copy first.)  The nops keep the VALU write of the
 // operands and the read of the results clear of the swap.
+// The max is taken inside the same asm block: a compiler-issued max of an
+// asm result would first quiet possible signalling NaNs (one more VALU op per
+// operand), which the swap of plain scores never produces.
 __device__ __forceinline__ float max_xor32(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return a;
 }
 
 // The same for lanes l and l ^ 16: v_permlane16_swap_b32 a, b swaps the odd
 // 16-lane rows of a with the even rows of b.
 __device__ __forceinline__ float max_xor16(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1\n\tv_max_f32 %0, %0, %1"
+               : "+v"(a), "+v"(b));
+  return a;
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0

@@ -26,10 +26,10 @@ struct DecodeArgs {
   const int32_t* cu;
   void* o;
   float* lse;
-  float* part_o;      // [waves + B*Hkv, Hq/Hkv, d] fp32 partial outputs
-  float* part_lse;    // [waves + B*Hkv, Hq/Hkv] fp32 partial logsumexps
+  float* part_o;      // [(ranges + B) * Hq, d] fp32 partial outputs
+  float* part_lse;    // [(ranges + B) * Hq] fp32 partial logsumexps
   int B, Hq, Hkv, d;
-  int waves;          // split-kernel waves (0: no keys to attend)
+  int ranges;         // key ranges of the split (0: no keys to attend)
   float scale;
   hipStream_t stream;
 };

@@ -244,6 +244,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   bool rescale = false;      // wave-uniform: some row of the wave has alpha != 1
   f32x4 s[kRB][2];           // scores of the current tile: item r of block kb = key 8c + 4kb + r
   bf16x8 pf[kRB];            // weights of the current tile, B operands of P.V
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) pf[rb] = bf16x8{};   // the first P.V adds nothing
 
   // S^T = K Q^T for the K tile at `kst`
   auto stage_s = [&](const char* kst) {
@@ -277,8 +279,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
         acc_o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rb], acc_o[rb][db], 0, 0, 0);
-      // keep few operand reads in flight (bounds register use)
-      if ((db & 1) == 1) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -358,8 +358,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   // explicit ones below, before the workgroup barriers).
   auto mblock = [&](const int j, const char* kread, const char* vread, char* kdst, char* vdst,
                     auto copy_tag) __attribute__((always_inline)) {
-    if (j >= 1) stage_pv(vread);
+    // (tile 0's P.V reads the zero-filled stage of tile -1 with zero weights:
+    // no branch, so both products share one scheduling region)
+    stage_pv(vread);
     stage_s(kread);
+    // LDS operand reads run two MFMA groups ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // V^T operands of blocks 0, 1
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // reads two blocks ahead
+      __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);   // MFMAs of block db
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // K operand
+      __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);   // MFMAs of one K operand
+    }
     if (decltype(copy_tag)::value) {
       issue(k_slice, j + kPD, k_voff, kdst);
       issue(v_slice, j + kPD - 1, v_voff, vdst);
@@ -412,6 +426,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     }
   };
   if (n_kv > 0) {
+    // tile -1's V stage (kNS - 1) holds zeros, written by plain stores; the
+    // first copy into it is issued in phase 2, after both groups' first P.V
+    static_assert(TILE_ELEMS * 2 == kThreads * 16 || TILE_ELEMS * 2 == kThreads * 8, "zero fill layout");
+    if (TILE_ELEMS * 2 == kThreads * 16)
+      store16(vS(kNS - 1) + tid * 16, u32x4{0u, 0u, 0u, 0u});
+    else
+      *reinterpret_cast<u32x2*>(vS(kNS - 1) + tid * 8) = u32x2{0u, 0u};
     if (group == 0) {
 #pragma unroll
       for (int t = 0; t < kPD; ++t) issue(k_slice, t, k_voff, kS(t));

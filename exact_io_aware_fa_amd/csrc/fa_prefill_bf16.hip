@@ -40,10 +40,11 @@
 //  * Softmax in the base-2 domain: p = 2^(s*c - m), c = scale*log2(e).  The
 //    reference max m is set by the row's first visible tile and moves only
 //    when a tile's max exceeds it by more than kRescaleSlack; any consistent
-//    reference gives the same O = sum p v / sum p.  Two row sums are kept:
-//    fp32 weights (for LSE) and the bf16-rounded weights the MFMA multiplies
-//    (to normalise O, so the rounding of P does not bias O).  The rare
-//    rescale of O is applied just before the next P.V.
+//    reference gives the same O = sum p v / sum p.  Each lane compares only
+//    the max of its own 8 scores with the row's threshold; the row max is
+//    reduced across lanes only when the reference moves.  One fp32 row sum
+//    normalises O and gives the LSE.  The rare rescale of O is applied just
+//    before the next P.V.
 #include <type_traits>
 
 #include "fa_common.h"
@@ -231,14 +232,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc_o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_ref[kRB], nmu[kRB], thr[kRB], l_part[kRB], l_rnd[kRB], alpha[kRB];
+  float m_ref[kRB], nmu[kRB], thr[kRB], l_part[kRB], alpha[kRB];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     m_ref[rb] = -INFINITY;   // reference max of the lane's row (base-2 domain), same in its 4 lanes
     nmu[rb] = 0.0f;          // -m_ref, or 0 while the row has seen no key
     thr[rb] = -INFINITY;     // raw score above which the reference must move
     l_part[rb] = 0.0f;       // fp32 weights of this lane's keys (for LSE)
-    l_rnd[rb] = 0.0f;        // bf16-rounded weights of this lane's keys (for O)
     alpha[rb] = 1.0f;        // pending rescale of acc_o (applied before the next P.V)
   }
   bool rescale = false;      // wave-uniform: some row of the wave has alpha != 1
@@ -291,7 +291,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   // more than kRescaleSlack, on a wave-uniform branch that is rarely taken.
   // (c > 0, so s*c > m + slack  <=>  s > (m + slack)/c.)
   auto stage_softmax = [&](const int j0, const bool masked) {
-    float mx[kRB];
+    float lm[kRB];             // max of this lane's 8 scores of each row block
+    bool need = false;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
       if (__builtin_expect(masked, 0)) {
@@ -304,37 +305,29 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[rb][kb][r] = 4 * kb + r <= lim_rel ? s[rb][kb][r] : -INFINITY;
       }
-      float m = s[rb][0][0];
+      float m = -INFINITY;     // (a -inf seed keeps the chain to plain v_max3_f32)
 #pragma unroll
-      for (int i = 1; i < 8; ++i) m = fmaxf(m, s[rb][i >> 2][i & 3]);
-      m = max_xor16(m);                        // the row's 32 keys sit in lanes j, j+16, j+32, j+48
-      mx[rb] = max_xor32(m);
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, s[rb][i >> 2][i & 3]);
+      lm[rb] = m;
+      need = need | (m > thr[rb]);
     }
-    if (j0 == 0) {
+    // Tile 0 sets every row's reference (thr = -inf there); later tiles move
+    // it only when some score exceeds thr, on a wave-uniform branch.  Only
+    // then is the row max reduced across the row's 4 lanes.
+    rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+    if (__builtin_expect(rescale, 0)) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {
-        m_ref[rb] = mx[rb] * c;
-        nmu[rb] = m_ref[rb] == -INFINITY ? 0.0f : -m_ref[rb];
-        thr[rb] = (m_ref[rb] + kRescaleSlack) / c;
-      }
-      rescale = false;
-    } else {
-      bool need = false;
-#pragma unroll
-      for (int rb = 0; rb < kRB; ++rb) need = need || mx[rb] > thr[rb];
-      rescale = __builtin_amdgcn_ballot_w64(need) != 0;
-      if (__builtin_expect(rescale, 0)) {
-#pragma unroll
-        for (int rb = 0; rb < kRB; ++rb) {
-          const bool up = mx[rb] > thr[rb];
-          const float m_new = up ? mx[rb] * c : m_ref[rb];
-          alpha[rb] = up ? fast_exp2(m_ref[rb] - m_new) : 1.0f;
-          m_ref[rb] = m_new;
-          nmu[rb] = -m_new;
-          thr[rb] = (m_new + kRescaleSlack) / c;
-          l_part[rb] *= alpha[rb];
-          l_rnd[rb] *= alpha[rb];
-        }
+        // the row's 32 keys sit in lanes j, j+16, j+32, j+48
+        const float mx = max_xor32(max_xor16(lm[rb]));
+        const bool up = mx > thr[rb];
+        const float m_new = up ? mx * c : m_ref[rb];
+        // a row's first reference: its sums and O are still 0 (alpha = 0)
+        alpha[rb] = up ? (m_ref[rb] == -INFINITY ? 0.0f : fast_exp2(m_ref[rb] - m_new)) : 1.0f;
+        m_ref[rb] = m_new;
+        nmu[rb] = up ? -m_new : nmu[rb];
+        thr[rb] = up ? (m_new + kRescaleSlack) / c : thr[rb];
+        l_part[rb] *= alpha[rb];
       }
     }
 #pragma unroll
@@ -343,13 +336,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          p[4 * kb + r] = fast_exp2(fmaf(s[rb][kb][r], c, nmu[rb]));
-          l_part[rb] += p[4 * kb + r];
-        }
-      pf[rb] = pack_bf16x8_sum(p, &l_rnd[rb]);
+        for (int r = 0; r < 4; ++r) p[4 * kb + r] = fast_exp2(fmaf(s[rb][kb][r], c, nmu[rb]));
+      l_part[rb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      const u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                       pack_bf16x2(p[6], p[7])};
+      pf[rb] = __builtin_bit_cast(bf16x8, w);
     }
   };
+
 
   // The MFMA block of tile j: P.V of tile j-1, S of tile j, and (group 0)
   // the copies of K_{j+kPD} and V_{j+kPD-1}.  The read and copy stages are
@@ -363,7 +357,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     stage_pv(vread);
     stage_s(kread);
     // LDS operand reads run two MFMA groups ahead of their use
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // V^T operands of blocks 0, 1
+#ifndef PREFILL_READ_AHEAD
+#define PREFILL_READ_AHEAD 2
+#endif
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PREFILL_READ_AHEAD, 0);   // V^T operands of the first blocks
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // reads two blocks ahead
@@ -459,16 +456,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     }
   }
 
-  // ---- epilogue: O = acc / l_rnd, LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
   // (the last tile's rescale was applied by the final P.V block)
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     float lt = l_part[rb] + wave_xor16(l_part[rb]);
     lt += wave_xor32(lt);
-    float lr = l_rnd[rb] + wave_xor16(l_rnd[rb]);
-    lr += wave_xor32(lr);
     const int row = wbase + 16 * rb + l16;
-    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     if (row < N) {
       uint16_t* dst = o + ((int64_t)b * N + row) * ((int64_t)Hq * D) + (int64_t)h * D + 4 * grp;
 #pragma unroll

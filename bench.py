@@ -13,6 +13,10 @@ Prints one JSON line.  `value` is the prefill throughput in TFLOP/s counted as
 4*B*Hq*N*Nk*d/2 (the causal half), measured with HIP events around each
 launch on the launch stream; the decode part is reported beside it in GB/s of
 algorithmic bytes (K and V cache, q, o, lse and cu_seqlens, each once).
+After the timed steps, a chunked variable-length prefill (16 sequences of
+2048-token chunks on caches of 0..14336 earlier tokens, fa_fwd_varlen) is timed
+on its own and reported as `roofline_varlen_prefill`, counting 4*d*Hq flops
+per visible (query, key) pair.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --pmc-pass      # one launch of each kernel plus a copy of known
@@ -120,6 +124,18 @@ def decode_bytes(cfg, total_len):
     return kv + qo + cfg.B * cfg.Hq * 4 + (cfg.B + 1) * 4
 
 
+def varlen_flops(cfg, q_lens, k_lens):
+    """4*d*Hq per visible (query, key) pair; causal is bottom-right per sequence."""
+    pairs = 0
+    for n, nk in zip(q_lens.tolist(), k_lens.tolist()):
+        if not cfg.causal:
+            pairs += n * nk
+        else:
+            # query i sees keys 0 .. i + nk - n (clipped to 0 .. nk - 1)
+            pairs += sum(max(0, min(nk, i + nk - n + 1)) for i in range(n))
+    return 4.0 * cfg.d * cfg.Hq * pairs
+
+
 def cpu_baseline(q, k, v, cfg):
     """The fp64 oracle on a bounded sample of the prefill workload: every 8th
     query row, all heads.  Reported as algorithmic TFLOP/s of the sample."""
@@ -224,6 +240,32 @@ def main():
     dbytes = decode_bytes(dcfg, total_len)
     gbs = dbytes / (dec_avg * 1e-3) / 1e9
 
+    # chunked variable-length prefill, timed on its own after the steps
+    vcfg = inputs.VARLEN_CHUNKED_BF16
+    vq, vk, vv, vcu_q, vcu_k, vq_lens, vk_lens = inputs.varlen_config_inputs(vcfg)
+    vqd, vkd, vvd = vq.to(dev), vk.to(dev), vv.to(dev)
+    vcuq, vcuk = vcu_q.to(dev), vcu_k.to(dev)
+    del vq, vk, vv
+    vo = torch.empty_like(vqd)
+    vl = torch.empty((vcfg.Hq, vqd.shape[0]), dtype=torch.float32, device=dev)
+    vmax_q, vmax_k = int(vq_lens.max()), int(vk_lens.max())
+
+    def varlen():
+        binding.fwd_varlen(vqd, vkd, vvd, vcuq, vcuk, vmax_q, vmax_k, vcfg.causal, vcfg.scale, out=vo, lse=vl)
+
+    for _ in range(args.warmup):
+        varlen()
+    torch.cuda.synchronize()
+    va, vb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    va.record()
+    for _ in range(K):
+        varlen()
+    vb.record()
+    torch.cuda.synchronize()
+    var_ms = va.elapsed_time(vb) / K
+    vflops = varlen_flops(vcfg, vq_lens, vk_lens)
+    vtflops = vflops / (var_ms * 1e-3) / 1e12
+
     pre_traffic = measured_traffic("prefill")
     dec_traffic = measured_traffic("decode")
     result = {
@@ -249,6 +291,9 @@ def main():
                        "sum_len": total_len, "max_len": max_len, "ms": round(dec_avg, 4),
                        "bytes_per_launch": dbytes, "GB/s": round(gbs, 1),
                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
+            "varlen_prefill": {"B": vcfg.B, "Hq": vcfg.Hq, "Hkv": vcfg.Hkv, "d": vcfg.d, "causal": vcfg.causal,
+                               "chunk": vcfg.chunk, "sum_q": int(vq_lens.sum()), "sum_k": int(vk_lens.sum()),
+                               "max_k": vmax_k, "ms": round(var_ms, 4), "flops_per_launch": vflops},
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -256,6 +301,9 @@ def main():
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                             "traffic": dec_traffic},
+        "roofline_varlen_prefill": {"bound": "mfma", "achieved": round(vtflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(vtflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                                    "traffic": None},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, pcfg)

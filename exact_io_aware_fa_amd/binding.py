@@ -16,7 +16,7 @@ _LIBNAME = "libfa.so"
 
 FA_F32, FA_BF16 = 0, 1
 FA_OK = 0
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lib = None
 
@@ -48,6 +48,8 @@ def load_library():
     p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p]
     lib.fa_fwd.restype = i32
+    lib.fa_fwd_varlen.argtypes = [i32, p, p, p, p, p, i32, i32, i32, i32, p, p, i32, i32, i32, i32, i32, f32, p]
+    lib.fa_fwd_varlen.restype = i32
     lib.fa_decode.argtypes = [i32, p, p, p, p, i32, p, p, i32, i32, i32, i32, f32, p, sz, p]
     lib.fa_decode.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -119,6 +121,40 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, scale: 
     st = lib.fa_fwd(_dtype_code(q), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(out),
                     _dev_ptr(lse), B, Hq, Hkv, N, Nk, d, 1 if causal else 0, float(scale),
                     _stream_handle(stream))
+    if st != FA_OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+               cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, causal: bool, scale: float,
+               out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """Varlen / chunked prefill.  q [total_q,Hq,d], k/v [total_k,Hkv,d] (bf16, packed),
+    cu_seqlens_q/k int32 [B+1] on the device -> (o [total_q,Hq,d], lse [Hq,total_q] fp32)."""
+    lib = load_library()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [total_q,Hq,d] and k, v [total_k,Hkv,d]")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    if dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
+                                                             tuple(v.shape)))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu.dtype != torch.int32 or cu.dim() != 1:
+            raise ValueError("%s must be a 1-D int32 tensor" % name)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B+1 entries")
+    B = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    st = lib.fa_fwd_varlen(_dtype_code(q), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(cu_seqlens_q),
+                           _dev_ptr(cu_seqlens_k), int(max_seqlen_q), int(max_seqlen_k), total_q, total_k,
+                           _dev_ptr(out), _dev_ptr(lse), B, Hq, Hkv, d, 1 if causal else 0, float(scale),
+                           _stream_handle(stream))
     if st != FA_OK:
         _raise(lib, st)
     return out, lse

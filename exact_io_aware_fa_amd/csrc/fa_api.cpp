@@ -136,6 +136,50 @@ FA_EXPORT fa_status_t fa_fwd(fa_dtype_t dtype, const void* q, const void* k, con
   return ok();
 }
 
+FA_EXPORT fa_status_t fa_fwd_varlen(fa_dtype_t dtype, const void* q, const void* k, const void* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int max_seqlen_q,
+                                    int max_seqlen_k, int total_q, int total_k, void* o, float* lse, int B, int Hq,
+                                    int Hkv, int d, int causal, float scale, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || total_q < 0 || total_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size (B=%d max_seqlen_q=%d max_seqlen_k=%d total_q=%d total_k=%d)", B,
+                max_seqlen_q, max_seqlen_k, total_q, total_k);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (d <= 0) return fail(FA_ERR_INVALID_ARG, "head dim d=%d", d);
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and positive (got %g)", (double)scale);
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "varlen prefill supports bf16 only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (B == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+  // work items and per-sequence buffer views use 32-bit integers
+  if ((int64_t)B * Hq * ((max_seqlen_q + 63) / 64) > INT32_MAX - 8)
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for 32-bit work indexing");
+  if (((int64_t)max_seqlen_q + 256) * Hq * d * 2 >= INT32_MAX ||
+      ((int64_t)max_seqlen_k + 256) * Hkv * d * 2 >= INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "one sequence of q or k/v exceeds 2 GiB");
+  if (!q || !o || !lse || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(FA_ERR_INVALID_ARG, "null q, o, lse or cu_seqlens pointer");
+  if (total_k > 0 && (!k || !v)) return fail(FA_ERR_INVALID_ARG, "null k or v pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+  const size_t q_bytes = (size_t)total_q * Hq * d * 2;
+  const size_t kv_bytes = (size_t)total_k * Hkv * d * 2;
+  const size_t lse_bytes = (size_t)Hq * total_q * sizeof(float);
+  if (overlaps(o, q_bytes, q, q_bytes) || overlaps(o, q_bytes, k, kv_bytes) || overlaps(o, q_bytes, v, kv_bytes) ||
+      overlaps(lse, lse_bytes, q, q_bytes) || overlaps(lse, lse_bytes, k, kv_bytes) ||
+      overlaps(lse, lse_bytes, v, kv_bytes) || overlaps(lse, lse_bytes, o, q_bytes))
+    return fail(FA_ERR_INVALID_ARG, "outputs alias inputs or each other");
+
+  fa::PrefillArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, causal != 0, scale,
+                    reinterpret_cast<hipStream_t>(stream), cu_seqlens_q, cu_seqlens_k, total_q};
+  const hipError_t e = fa::launch_prefill_bf16(a);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 FA_EXPORT size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen_k <= 0 || Hq % Hkv != 0) return 0;
   return decode_layout(B, Hq, Hkv, d, max_seqlen_k).bytes;

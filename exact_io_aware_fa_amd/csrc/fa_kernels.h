@@ -13,10 +13,15 @@ struct PrefillArgs {
   const void* v;
   void* o;
   float* lse;
-  int B, Hq, Hkv, N, Nk, d;
+  int B, Hq, Hkv, N, Nk, d;   // N, Nk: the lengths, or (varlen) upper bounds of them
   bool causal;
   float scale;
   hipStream_t stream;
+  // varlen (bf16 only): packed sequences given by device cu_seqlens; null for
+  // the fixed-length [B, N, H, d] layout
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int total_q = 0;
 };
 
 struct DecodeArgs {

@@ -88,11 +88,14 @@ __device__ __forceinline__ int swz_v(int row) {
   return ((row & 3) << (CPR >= 16 ? 2 : 1)) ^ (((row >> 3) & 1) << 1);
 }
 
-template <int D, bool CAUSAL>
+// VARLEN: q/o are packed [total_q, Hq, d] and k/v [total_k, Hkv, d], sequence
+// b owning rows cu_q[b]..cu_q[b+1]-1 and cu_k[b]..cu_k[b+1]-1; LSE is
+// [Hq, total_q].  N_arg / Nk_arg are then upper bounds that size the grid.
+template <int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int N, int Nk, int Hq, int Hkv, float c,
-    int n_qtiles, int n_work) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int N_arg, int Nk_arg, int Hq, int Hkv, float c,
+    int n_qtiles, int n_work, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int total_q) {
   constexpr int DT = D / 32;                // MFMA k-steps of S^T = K Q^T (32 head-dim values each)
   constexpr int DB = D / 16;                // 16-wide head-dim blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -136,6 +139,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const int h = g * G + hig;
   const int q0 = qt * kBR;
 
+  // ---- this sequence's extents and first rows
+  int N = N_arg, Nk = Nk_arg;
+  int64_t q_row0 = (int64_t)b * N_arg, k_row0 = (int64_t)b * Nk_arg;
+  int64_t lse_row0 = ((int64_t)b * Hq + h) * N_arg;    // LSE of query row 0 (rows contiguous)
+  if (VARLEN) {
+    const int qs = cu_q[b], ks = cu_k[b];
+    N = cu_q[b + 1] - qs;
+    Nk = cu_k[b + 1] - ks;
+    q_row0 = qs;
+    k_row0 = ks;
+    lse_row0 = (int64_t)h * total_q + qs;
+    if (q0 >= N) return;                                // the tile lies past the sequence
+  }
+
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int lane = tid & 63;
@@ -148,9 +165,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
   const __amdgpu_buffer_rsrc_t q_rsrc =
-      make_rsrc(q + ((int64_t)b * N * Hq + h) * D, (uint32_t)((N - 1) * Hq + 1) * D * 2);
-  const uint16_t* k_slice = k + ((int64_t)b * Nk * Hkv + g) * D;
-  const uint16_t* v_slice = v + ((int64_t)b * Nk * Hkv + g) * D;
+      make_rsrc(q + (q_row0 * Hq + h) * D, (uint32_t)((N - 1) * Hq + 1) * D * 2);
+  const uint16_t* k_slice = k + (k_row0 * Hkv + g) * D;
+  const uint16_t* v_slice = v + (k_row0 * Hkv + g) * D;
   const uint32_t kv_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * Hkv + 1) * D * 2 : 0u;
 
   // ---- Q -> registers (B operands of S^T = K Q^T): lane (row j, group c)
@@ -465,7 +482,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const int row = wbase + 16 * rb + l16;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
     if (row < N) {
-      uint16_t* dst = o + ((int64_t)b * N + row) * ((int64_t)Hq * D) + (int64_t)h * D + 4 * grp;
+      uint16_t* dst = o + (q_row0 + row) * ((int64_t)Hq * D) + (int64_t)h * D + 4 * grp;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const f32x4 a = acc_o[rb][db];
@@ -475,28 +492,32 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
         *reinterpret_cast<u32x2*>(dst + 16 * db) = w;
       }
       if (grp == 0)
-        lse[((int64_t)b * Hq + h) * N + row] = lt > 0.0f ? (m_ref[rb] + fast_log2(lt)) * kLn2 : -INFINITY;
+        lse[lse_row0 + row] = lt > 0.0f ? (m_ref[rb] + fast_log2(lt)) * kLn2 : -INFINITY;
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool VARLEN>
 hipError_t launch(const PrefillArgs& a) {
   const int n_qtiles = (a.N + kBR - 1) / kBR;
   const int64_t n_work = (int64_t)a.B * a.Hq * n_qtiles;
   if (n_work == 0) return hipSuccess;
   const int64_t grid = (n_work + 7) / 8 * 8;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                     a.lse, a.N, a.Nk, a.Hq, a.Hkv, a.scale * kLog2e, n_qtiles, (int)n_work);
+                     a.lse, a.N, a.Nk, a.Hq, a.Hkv, a.scale * kLog2e, n_qtiles, (int)n_work, a.cu_q, a.cu_k,
+                     a.total_q);
   return hipGetLastError();
+}
+
+template <bool VARLEN>
+hipError_t dispatch(const PrefillArgs& a) {
+  if (a.d == 64) return a.causal ? launch<64, true, VARLEN>(a) : launch<64, false, VARLEN>(a);
+  return a.causal ? launch<128, true, VARLEN>(a) : launch<128, false, VARLEN>(a);
 }
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a) {
-  if (a.d == 64) return a.causal ? launch<64, true>(a) : launch<64, false>(a);
-  return a.causal ? launch<128, true>(a) : launch<128, false>(a);
-}
+hipError_t launch_prefill_bf16(const PrefillArgs& a) { return a.cu_q ? dispatch<true>(a) : dispatch<false>(a); }
 
 }  // namespace fa

@@ -75,6 +75,33 @@ DECODE_VARLEN_BF16 = DecodeConfig("varlen KV-cache decode bf16 32 seqs L512-3276
 PREFILL_CONFIGS = (SINGLE_HEAD_F32, BERT_LARGE_BF16, GPT2_CAUSAL_BF16, LLAMA70B_GQA_BF16)
 
 
+@dataclass(frozen=True)
+class VarlenConfig:
+    """Chunked prefill: B sequences, each a chunk of `chunk` new query tokens
+    appended to a cache of ctx_lo..ctx_hi (inclusive, uniform) earlier tokens,
+    so N_b = chunk and Nk_b = ctx_b + chunk."""
+    name: str
+    dtype: torch.dtype
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    chunk: int
+    ctx_lo: int
+    ctx_hi: int
+
+    @property
+    def scale(self) -> float:
+        return fp32_scale(self.d)
+
+
+# Llama2-70B-shaped heads; chunks and cache lengths up to the 16K context the
+# pages' Llama2-70B discussion works within (ai6s.net page, section "the data").
+VARLEN_CHUNKED_BF16 = VarlenConfig("chunked prefill bf16 16 seqs: 2048-token chunks on 0-14336 cached tokens, "
+                                   "Hq64 Hkv8 d128, causal", torch.bfloat16, 16, 64, 8, 128, True, 2048, 0, 14336)
+
+
 def _normal(g: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
     return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype)
 
@@ -133,3 +160,26 @@ def decode_config_inputs(cfg: DecodeConfig, seed: int = 0):
     lens = decode_lengths(cfg.B, cfg.len_lo, cfg.len_hi, g)
     q, kc, vc, cu = decode_inputs(lens, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, g=g)
     return q, kc, vc, cu, lens
+
+
+def varlen_inputs(q_lens, k_lens, Hq: int, Hkv: int, d: int, dtype: torch.dtype = torch.bfloat16,
+                  seed: int = 0, g: torch.Generator | None = None):
+    """Packed Q [sum(q_lens),Hq,d], K/V [sum(k_lens),Hkv,d] and cu_seqlens_q/k int32 [B+1]."""
+    if g is None:
+        g = torch.Generator().manual_seed(seed)
+    q_lens = torch.as_tensor(q_lens, dtype=torch.int64)
+    k_lens = torch.as_tensor(k_lens, dtype=torch.int64)
+    q = _normal(g, (int(q_lens.sum()), Hq, d), dtype)
+    k = _normal(g, (int(k_lens.sum()), Hkv, d), dtype)
+    v = _normal(g, (int(k_lens.sum()), Hkv, d), dtype)
+    return q, k, v, cu_from_lengths(q_lens), cu_from_lengths(k_lens)
+
+
+def varlen_config_inputs(cfg: VarlenConfig, seed: int = 0):
+    """The cached lengths are drawn first from the same generator, then Q, K, V."""
+    g = torch.Generator().manual_seed(seed)
+    ctx = torch.randint(cfg.ctx_lo, cfg.ctx_hi + 1, (cfg.B,), generator=g, dtype=torch.int64)
+    q_lens = torch.full((cfg.B,), cfg.chunk, dtype=torch.int64)
+    k_lens = ctx + cfg.chunk
+    q, k, v, cu_q, cu_k = varlen_inputs(q_lens, k_lens, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, g=g)
+    return q, k, v, cu_q, cu_k, q_lens, k_lens

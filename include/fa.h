@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
     FA_OK = 0,
@@ -84,6 +84,44 @@ fa_status_t fa_fwd(fa_dtype_t dtype,
                    void *o, float *lse,
                    int B, int Hq, int Hkv, int N, int Nk, int d,
                    int causal, float scale, void *stream);
+
+/*
+ * Variable-length and chunked prefill: B packed sequences, sequence b having
+ * N_b query rows and Nk_b keys, N_b <= Nk_b typical for a chunk of new tokens
+ * appended to a cache of Nk_b - N_b earlier ones (ai6s.net page, section
+ * "what ops-transformer adds", third item: attend to the real lengths only;
+ * second item: the causal mask inside the blockwise softmax).
+ *
+ *   q            [total_q, Hq,  d]  bf16, sequence b owns rows
+ *                                   cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   k, v         [total_k, Hkv, d]  bf16, sequence b owns rows
+ *                                   cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *   cu_seqlens_q,
+ *   cu_seqlens_k [B+1]              int32, DEVICE pointers; cu[0] == 0,
+ *                                   non-decreasing, cu_seqlens_q[B] == total_q,
+ *                                   cu_seqlens_k[B] == total_k.  These cannot be
+ *                                   checked without a synchronisation, so they
+ *                                   are preconditions, and so are
+ *                                   N_b <= max_seqlen_q and Nk_b <= max_seqlen_k.
+ *   max_seqlen_q,
+ *   max_seqlen_k                    host-side upper bounds on the lengths
+ *   o            [total_q, Hq, d]   bf16 output
+ *   lse          [Hq, total_q]      fp32 output, natural-log logsumexp
+ *   causal != 0: bottom-right alignment within each sequence, key j of
+ *                sequence b is visible to its query i iff j <= i + (Nk_b - N_b).
+ *   A row with no visible key gets O = 0 and LSE = -inf; a sequence with no
+ *   query rows writes nothing.  B == 0 or total_q == 0 is a no-op.
+ *   dtype must be FA_BF16 (FA_F32 returns FA_ERR_UNSUPPORTED).
+ *
+ * Returns FA_OK or an error status (see above); nothing is enqueued on error.
+ */
+fa_status_t fa_fwd_varlen(fa_dtype_t dtype,
+                          const void *q, const void *k, const void *v,
+                          const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                          int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                          void *o, float *lse,
+                          int B, int Hq, int Hkv, int d,
+                          int causal, float scale, void *stream);
 
 /*
  * Decode forward over a packed, variable-length KV cache (one new query token

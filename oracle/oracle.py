@@ -153,6 +153,39 @@ def attention(q, k, v, causal: bool, scale: float, nthreads: int = 0, lib=None):
     return o, lse
 
 
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, causal: bool, scale: float, nthreads: int = 0,
+                     lib=None):
+    """Variable-length prefill: the definition applied to each sequence on its own.
+
+    q [total_q,Hq,d], k/v [total_k,Hkv,d] packed; sequence b owns the q rows
+    cu_seqlens_q[b]..cu_seqlens_q[b+1]-1 and the k/v rows cu_seqlens_k[b]..
+    cu_seqlens_k[b+1]-1 and is attended as a batch of one (bottom-right causal
+    alignment within the sequence).  Source: ai6s.net page, section "what
+    ops-transformer adds", second item (causal mask) and third item (attend to
+    the real lengths only).  Returns (o [total_q,Hq,d] float64, lse [Hq,total_q]
+    float64); rows of no sequence stay 0.
+    """
+    cq = [int(x) for x in torch.as_tensor(cu_seqlens_q).cpu().tolist()]
+    ck = [int(x) for x in torch.as_tensor(cu_seqlens_k).cpu().tolist()]
+    if len(cq) != len(ck) or not cq:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both have B+1 entries")
+    total_q, Hq, d = q.shape
+    total_k = k.shape[0]
+    if cq[-1] > total_q or ck[-1] > total_k:
+        raise ValueError("cu_seqlens end past the packed tensors")
+    o = np.zeros((total_q, Hq, d), dtype=np.float64)
+    lse = np.zeros((Hq, total_q), dtype=np.float64)
+    for b in range(len(cq) - 1):
+        qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if qe == qs:
+            continue
+        ob, lb = attention(q[qs:qe].unsqueeze(0), k[ks:ke].unsqueeze(0), v[ks:ke].unsqueeze(0), causal, scale,
+                           nthreads, lib)
+        o[qs:qe] = ob[0]
+        lse[:, qs:qe] = lb[0]
+    return o, lse
+
+
 def decode_rows(q, k_cache, v_cache, cu_seqlens, scale: float, rows, nthreads: int = 0,
                 lib=None):
     """Decode attention for selected (b, h) pairs.

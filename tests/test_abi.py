@@ -32,7 +32,7 @@ def _no_gpu():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
+    for n in ("fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
               "fa_last_error", "fa_abi_version"):
         assert n in names
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(fa_lib):
 
 
 def test_abi_version_and_status_names(fa_lib):
-    assert fa_lib.fa_abi_version() == 1
+    assert fa_lib.fa_abi_version() == 2
     names = [fa_lib.fa_status_str(s).decode() for s in range(5)]
     assert names == ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
                      "FA_ERR_HIP"]
@@ -81,6 +81,46 @@ def test_fwd_validation(fa_lib, kwargs, status):
         assert fa_lib.fa_last_error().decode() != ""
     else:
         assert fa_lib.fa_last_error().decode() == ""
+
+
+def _fwd_varlen(lib, dtype=BF16, ptr=None, cu=None, max_q=4, max_k=6, total_q=8, total_k=12, B=2, Hq=2,
+                Hkv=1, d=64, causal=1, scale=0.125):
+    return lib.fa_fwd_varlen(dtype, ptr, ptr, ptr, cu, cu, max_q, max_k, total_q, total_k, ptr, ptr, B, Hq, Hkv, d,
+                             causal, scale, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=F32), FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), FA_ERR_INVALID_ARG),
+    (dict(B=-1), FA_ERR_INVALID_ARG),
+    (dict(max_q=-1), FA_ERR_INVALID_ARG),
+    (dict(max_k=-1), FA_ERR_INVALID_ARG),
+    (dict(total_q=-1), FA_ERR_INVALID_ARG),
+    (dict(total_k=-1), FA_ERR_INVALID_ARG),
+    (dict(Hq=3, Hkv=2), FA_ERR_INVALID_ARG),
+    (dict(d=96), FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), FA_ERR_INVALID_ARG),
+    (dict(), FA_ERR_INVALID_ARG),                       # null pointers with work to do
+    (dict(B=0), FA_OK),                                  # no work: nothing touched
+    (dict(total_q=0), FA_OK),
+    (dict(max_q=0), FA_OK),
+])
+def test_fwd_varlen_validation(fa_lib, kwargs, status):
+    st = _fwd_varlen(fa_lib, **kwargs)
+    assert st == status
+    if status != FA_OK:
+        assert fa_lib.fa_last_error().decode() != ""
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device addresses; CPU-only check")
+def test_fwd_varlen_alignment_and_aliasing_rejected(fa_lib):
+    q, k, v, cu, o, lse = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000, 0x60000
+    args = lambda q_, cu_, o_: fa_lib.fa_fwd_varlen(BF16, q_, k, v, cu_, cu_, 4, 6, 8, 12, o_, lse, 2, 2, 1, 64, 1,
+                                                    0.125, None)
+    assert args(q + 2, cu, o) == FA_ERR_INVALID_ARG and "aligned" in fa_lib.fa_last_error().decode()
+    assert args(q, cu + 2, o) == FA_ERR_INVALID_ARG and "cu_seqlens" in fa_lib.fa_last_error().decode()
+    assert args(q, cu, q) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
 
 
 def _decode(lib, dtype=BF16, ptr=None, cu=None, max_len=100, B=2, Hq=8, Hkv=1, d=128,

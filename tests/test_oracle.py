@@ -103,6 +103,68 @@ def test_brute_force_tiny(shape, causal):
     _close(lse, blse, 1e-12)
 
 
+# ------------------------------------------------- variable-length prefill
+
+VARLEN_TINY = [
+    # (q_lens, k_lens): chunks shorter than their caches, an empty chunk, a
+    # chunk with no cache rows, single rows
+    ((3, 0, 2, 1, 4), (5, 4, 0, 1, 4)),
+    ((1, 6), (9, 6)),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("lens", VARLEN_TINY)
+def test_varlen_brute_force_tiny(lens, causal):
+    """Each packed sequence equals the brute force of that sequence alone
+    (bottom-right causal within the sequence), in the [total_q,Hq,d] / [Hq,total_q] layouts."""
+    q_lens, k_lens = lens
+    Hq, Hkv, d = 4, 2, 4
+    q, k, v, cu_q, cu_k = inputs.varlen_inputs(q_lens, k_lens, Hq, Hkv, d, torch.float64, seed=len(q_lens) + causal)
+    scale = inputs.fp32_scale(d)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal, scale)
+    cq, ck = cu_q.tolist(), cu_k.tolist()
+    for b in range(len(q_lens)):
+        qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        if qe == qs:
+            continue
+        if ke == ks:        # no keys: O = 0, LSE = -inf
+            assert np.all(o[qs:qe] == 0.0) and np.all(lse[:, qs:qe] == -math.inf)
+            continue
+        bo, blse = brute.attention([q[qs:qe].tolist()], [k[ks:ke].tolist()], [v[ks:ke].tolist()], causal, scale)
+        _close(o[qs:qe], np.asarray(bo[0]), 1e-12)
+        _close(lse[:, qs:qe], np.asarray(blse[0]), 1e-12)
+
+
+def test_varlen_equal_lengths_match_batched():
+    """Packing B equal-length sequences gives the batched [B,N,H,d] result, with
+    LSE [B,Hq,N] laid out as [Hq, B*N]."""
+    B, N, Nk, Hq, Hkv, d = 3, 5, 9, 4, 2, 8
+    g = torch.Generator().manual_seed(11)
+    q, k, v = _randn(g, B, N, Hq, d), _randn(g, B, Nk, Hkv, d), _randn(g, B, Nk, Hkv, d)
+    scale = inputs.fp32_scale(d)
+    for causal in (False, True):
+        ro, rl = oracle.attention(q, k, v, causal, scale)
+        o, lse = oracle.attention_varlen(q.reshape(B * N, Hq, d), k.reshape(B * Nk, Hkv, d),
+                                         v.reshape(B * Nk, Hkv, d), inputs.cu_from_lengths([N] * B),
+                                         inputs.cu_from_lengths([Nk] * B), causal, scale)
+        _close(o, ro.reshape(B * N, Hq, d), 0.0)
+        _close(lse, rl.transpose(1, 0, 2).reshape(Hq, B * N), 0.0)
+
+
+def test_varlen_other_sequences_have_no_effect():
+    q, k, v, cu_q, cu_k = inputs.varlen_inputs((4, 3), (6, 5), 2, 1, 8, torch.float64, seed=3)
+    scale = inputs.fp32_scale(8)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, True, scale)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[:4] *= 7.0
+    k2[:6] += 3.0
+    v2[:6] -= 5.0
+    o2, lse2 = oracle.attention_varlen(q2, k2, v2, cu_q, cu_k, True, scale)
+    assert np.array_equal(o[4:], o2[4:]) and np.array_equal(lse[:, 4:], lse2[:, 4:])
+    assert not np.array_equal(o[:4], o2[:4])
+
+
 # ------------------------------------------------- reduction to library routines
 
 @pytest.mark.parametrize("Hq,Hkv,N,d", [(4, 4, 33, 16), (8, 2, 40, 64), (6, 3, 65, 128)])

@@ -354,3 +354,90 @@ def test_decode_matches_single_query_prefill():
                          vc[None, s:s + L].contiguous(), False, inputs.fp32_scale(128))
         assert (o[b].float() - op[0, 0].float()).abs().max() <= 1e-2
         assert (lse[b] - lp[0, :, 0]).abs().max() <= 1e-3
+
+
+# ------------------------------------------------- variable-length / chunked prefill
+
+def gpu_fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, causal, scale):
+    o, lse = binding.fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu_q.cuda(), cu_k.cuda(), max_q, max_k,
+                                causal, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+VARLEN_CASES = [
+    # (q_lens, k_lens, Hq, Hkv): a single row; a chunk on a longer cache; an
+    # empty chunk; a square ragged sequence; a chunk with no keys; a short chunk
+    # on a long cache
+    ((1, 37, 0, 401, 200, 64), (1, 300, 50, 401, 0, 1000), 8, 2),
+    # query-tile boundaries (384 rows per workgroup) and key-tile tails
+    ((384, 385, 767), (384, 1000, 767), 4, 4),
+]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=["mixed", "tile_edges"])
+def test_varlen_prefill(case, causal, d):
+    q_lens, k_lens, Hq, Hkv = case
+    _say("case: varlen q_lens=%s k_lens=%s Hq=%d Hkv=%d d=%d causal=%s" % (q_lens, k_lens, Hq, Hkv, d, causal))
+    q, k, v, cu_q, cu_k = inputs.varlen_inputs(q_lens, k_lens, Hq, Hkv, d, torch.bfloat16, seed=d + causal)
+    scale = inputs.fp32_scale(d)
+    o, lse = gpu_fwd_varlen(q, k, v, cu_q, cu_k, max(q_lens), max(k_lens), causal, scale)
+    ro, rl = oracle.attention_varlen(q, k, v, cu_q, cu_k, causal, scale)
+    assert_close(o, ro, 1e-2, "O")
+    assert_close(lse, rl, 1e-3, "LSE")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_varlen_equal_lengths_match_fixed_length_bitwise(causal):
+    """Packed equal-length sequences give the fixed-length launch's results bit for bit."""
+    B, N, Nk, Hq, Hkv, d = 3, 500, 700, 8, 2, 128
+    q, k, v = inputs.prefill_inputs(B, N, Nk, Hq, Hkv, d, torch.bfloat16, seed=5)
+    scale = inputs.fp32_scale(d)
+    o, lse = gpu_fwd(q, k, v, causal, scale)
+    vo, vl = gpu_fwd_varlen(q.reshape(B * N, Hq, d), k.reshape(B * Nk, Hkv, d), v.reshape(B * Nk, Hkv, d),
+                            inputs.cu_from_lengths([N] * B), inputs.cu_from_lengths([Nk] * B), N, Nk, causal, scale)
+    assert torch.equal(vo, o.reshape(B * N, Hq, d))
+    assert torch.equal(vl, lse.transpose(0, 1).reshape(Hq, B * N))
+
+
+def test_varlen_other_sequences_have_no_effect_bitwise():
+    """NaN in every row of the other sequences leaves a sequence's result unchanged
+    bit for bit: its workgroups read only its own rows."""
+    q_lens, k_lens = (300, 129, 512), (900, 129, 700)
+    q, k, v, cu_q, cu_k = inputs.varlen_inputs(q_lens, k_lens, 8, 2, 128, torch.bfloat16, seed=9)
+    scale = inputs.fp32_scale(128)
+    o, lse = gpu_fwd_varlen(q, k, v, cu_q, cu_k, 512, 900, True, scale)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    q2[:300] = float("nan")
+    q2[429:] = float("nan")
+    k2[:900] = float("nan")
+    k2[1029:] = float("nan")
+    v2[:900] = float("nan")
+    v2[1029:] = float("nan")
+    o2, lse2 = gpu_fwd_varlen(q2, k2, v2, cu_q, cu_k, 512, 900, True, scale)
+    assert torch.equal(o[300:429], o2[300:429])
+    assert torch.equal(lse[:, 300:429], lse2[:, 300:429])
+
+
+def test_varlen_chunked_workload_full_size_sampled():
+    """The chunked-prefill workload the benchmark times, at full size; the oracle
+    checks sampled rows (first, last and random rows of every sequence) one by one."""
+    cfg = inputs.VARLEN_CHUNKED_BF16
+    _say("case: %s (sampled rows)" % cfg.name)
+    q, k, v, cu_q, cu_k, q_lens, k_lens = inputs.varlen_config_inputs(cfg)
+    o, lse = gpu_fwd_varlen(q, k, v, cu_q, cu_k, int(q_lens.max()), int(k_lens.max()), cfg.causal, cfg.scale)
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    rng = np.random.default_rng(1)
+    cq, ck = cu_q.tolist(), cu_k.tolist()
+    for b in range(cfg.B):
+        qs, qe, ks, ke = cq[b], cq[b + 1], ck[b], ck[b + 1]
+        n = qe - qs
+        ii = np.unique(np.concatenate([[0, n - 1], rng.integers(0, n, 4)]))
+        hh = rng.integers(0, cfg.Hq, ii.size)
+        rows = np.stack([np.zeros_like(ii), hh, ii], axis=1)
+        ro, rl = oracle.attention_rows(q[qs:qe].unsqueeze(0), k[ks:ke].unsqueeze(0), v[ks:ke].unsqueeze(0),
+                                       cfg.causal, cfg.scale, rows)
+        assert_close(o[qs + ii, hh], ro, 1e-2, "O (sequence %d, sampled rows)" % b)
+        assert_close(lse[hh, qs + ii], rl, 1e-3, "LSE (sequence %d, sampled rows)" % b)

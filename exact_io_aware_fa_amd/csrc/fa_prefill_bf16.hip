@@ -125,19 +125,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     return reinterpret_cast<char*>(st == 0 ? sV0 : st == 1 ? sV1 : st == 2 ? sV2 : sV3);
   };
 
+  // Work items in the order (kv head, batch, query tile, query head in the
+  // group): a contiguous eighth of the items runs on one XCD, so with 8 kv
+  // heads each XCD holds one kv head of every sequence (equal work even when
+  // the sequences' lengths differ), and the heads of one group, which read
+  // the same K/V, run side by side on one L2.
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   if (logical >= n_work) return;
   const int G = Hq / Hkv;
+  const int n_batch = n_work / (Hq * n_qtiles);
   int rest = logical;
   const int hig = rest % G;
   rest /= G;
   const int qrank = rest % n_qtiles;
   rest /= n_qtiles;
-  const int g = rest % Hkv;
-  const int b = rest / Hkv;
-  const int qt = CAUSAL ? (n_qtiles - 1 - qrank) : qrank;   // heaviest causal tiles first
+  const int b = rest % n_batch;
+  const int g = rest / n_batch;
   const int h = g * G + hig;
-  const int q0 = qt * kBR;
 
   // ---- this sequence's extents and first rows
   int N = N_arg, Nk = Nk_arg;
@@ -150,8 +154,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     q_row0 = qs;
     k_row0 = ks;
     lse_row0 = (int64_t)h * total_q + qs;
-    if (q0 >= N) return;                                // the tile lies past the sequence
+    if (qrank * kBR >= N) return;                       // the tile lies before the sequence
   }
+  // Query tiles are aligned to the end of the sequence: tile qrank holds rows
+  // N-(qrank+1)*kBR .. N-qrank*kBR-1, so a partial tile (rows below 0 are
+  // absent) holds the first rows, which see the fewest keys under the causal
+  // mask, and tile 0, the heaviest, is scheduled first.
+  const int q0 = N - (qrank + 1) * kBR;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -171,11 +180,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   const uint32_t kv_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * Hkv + 1) * D * 2 : 0u;
 
   // ---- Q -> registers (B operands of S^T = K Q^T): lane (row j, group c)
-  // holds head-dim 32t + 8c..+7 of row 16rb + j; rows past N read 0
+  // holds head-dim 32t + 8c..+7 of row 16rb + j; absent rows (below 0) get an
+  // offset past any slice (slices are under 2 GiB) and read 0
   bf16x8 qf[kRB][DT];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
-    const uint32_t off = (uint32_t)(wbase + 16 * rb + l16) * q_row_bytes + grp * 16;
+    const int row = wbase + 16 * rb + l16;
+    const uint32_t off = row >= 0 ? (uint32_t)row * q_row_bytes + grp * 16 : 0x80000000u;
 #pragma unroll
     for (int t = 0; t < DT; ++t) qf[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(q_rsrc, off + t * 64));
   }
@@ -183,14 +194,15 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   // ---- KV tiles this workgroup needs, and where this wave's masked suffix starts
   int n_kv = (Nk + kBC - 1) / kBC;
   if (CAUSAL) {
-    const int last_key = min(q0 + kBR - 1, N - 1) + offs;
+    const int last_key = N - qrank * kBR - 1 + offs;       // the tile's last row's last key
     n_kv = last_key < 0 ? 0 : min(n_kv, last_key / kBC + 1);
   }
   // tile j needs no mask for this wave iff j*kBC + kBC-1 < Nk and, when
-  // causal, j*kBC + kBC-1 <= wbase + offs (the wave's first row sees it all)
+  // causal, j*kBC + kBC-1 <= max(wbase, 0) + offs (the wave's first present
+  // row sees it all; absent rows are never stored, so what they see is moot)
   int n_clean = Nk / kBC;
   if (CAUSAL) {
-    const int d0 = wbase + offs - (kBC - 1);
+    const int d0 = max(wbase, 0) + offs - (kBC - 1);
     n_clean = min(n_clean, d0 < 0 ? 0 : d0 / kBC + 1);
   }
   n_clean = min(n_clean, n_kv);
@@ -481,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     lt += wave_xor32(lt);
     const int row = wbase + 16 * rb + l16;
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    if (row < N) {
+    if (row >= 0) {                                  // (every row is below N)
       uint16_t* dst = o + (q_row0 + row) * ((int64_t)Hq * D) + (int64_t)h * D + 4 * grp;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {

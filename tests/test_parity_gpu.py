@@ -368,8 +368,8 @@ def gpu_fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, causal, scale):
 VARLEN_CASES = [
     # (q_lens, k_lens, Hq, Hkv): a single row; a chunk on a longer cache; an
     # empty chunk; a square ragged sequence; a chunk with no keys; a short chunk
-    # on a long cache
-    ((1, 37, 0, 401, 200, 64), (1, 300, 50, 401, 0, 1000), 8, 2),
+    # on a long cache; more queries than keys (causal: the leading rows see none)
+    ((1, 37, 0, 401, 200, 64, 530), (1, 300, 50, 401, 0, 1000, 77), 8, 2),
     # query-tile boundaries (384 rows per workgroup) and key-tile tails
     ((384, 385, 767), (384, 1000, 767), 4, 4),
 ]

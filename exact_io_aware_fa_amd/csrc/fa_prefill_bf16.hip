@@ -320,11 +320,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   // more than kRescaleSlack, on a wave-uniform branch that is rarely taken.
   // (c > 0, so s*c > m + slack  <=>  s > (m + slack)/c.)
   auto stage_softmax = [&](const int j0, const bool masked) {
-    float lm[kRB];             // max of this lane's 8 scores of each row block
-    bool need = false;
+    if (__builtin_expect(masked, 0)) {
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      if (__builtin_expect(masked, 0)) {
+      for (int rb = 0; rb < kRB; ++rb) {
         // last visible key of this lane's row; item r of block kb holds key
         // j0 + 8grp + 4kb + r
         const int lim = CAUSAL ? min(Nk - 1, wbase + 16 * rb + l16 + offs) : Nk - 1;
@@ -334,16 +332,25 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) s[rb][kb][r] = 4 * kb + r <= lim_rel ? s[rb][kb][r] : -INFINITY;
       }
+    }
+    // (the threshold tests follow the one masking branch in a single block,
+    // and each compare is balloted on its own: a ballot of a compare is the
+    // compare's lane mask, while a ballot of an OR of compares rebuilds a
+    // per-lane bool first)
+    float lm[kRB];             // max of this lane's 8 scores of each row block
+    uint64_t need = 0;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
       float m = -INFINITY;     // (a -inf seed keeps the chain to plain v_max3_f32)
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, s[rb][i >> 2][i & 3]);
       lm[rb] = m;
-      need = need | (m > thr[rb]);
+      need |= __builtin_amdgcn_ballot_w64(m > thr[rb]);
     }
     // Tile 0 sets every row's reference (thr = -inf there); later tiles move
     // it only when some score exceeds thr, on a wave-uniform branch.  Only
     // then is the row max reduced across the row's 4 lanes.
-    rescale = __builtin_amdgcn_ballot_w64(need) != 0;
+    rescale = need != 0;
     if (__builtin_expect(rescale, 0)) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb) {

@@ -16,7 +16,11 @@ algorithmic bytes (K and V cache, q, o, lse and cu_seqlens, each once).
 After the timed steps, a chunked variable-length prefill (16 sequences of
 2048-token chunks on caches of 0..14336 earlier tokens, fa_fwd_varlen) is timed
 on its own and reported as `roofline_varlen_prefill`, counting 4*d*Hq flops
-per visible (query, key) pair.
+per visible (query, key) pair.  Then the decode workload on a paged cache of
+64-row blocks, with each sequence's new K/V row appended in the same call
+(fa_decode_paged), is timed and reported as `roofline_decode_paged` in GB/s of
+algorithmic bytes (the cached rows, the new rows read and written, q, o, lse,
+the lengths and the block-table entries used, each once).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --pmc-pass      # one launch of each kernel plus a copy of known
@@ -122,6 +126,18 @@ def decode_bytes(cfg, total_len):
     kv = 2 * total_len * cfg.Hkv * cfg.d * 2
     qo = 2 * cfg.B * cfg.Hq * cfg.d * 2
     return kv + qo + cfg.B * cfg.Hq * 4 + (cfg.B + 1) * 4
+
+
+PAGED_BLOCK = 64                   # rows per block of the paged decode workload
+
+
+def paged_decode_bytes(cfg, lens, block_size):
+    """Algorithmic bytes of one paged decode step with the new rows appended."""
+    row = cfg.Hkv * cfg.d * 2                      # one K (or V) row of all kv heads, bf16
+    total = int(lens.sum())
+    blocks = sum((int(L) + 1 + block_size - 1) // block_size for L in lens.tolist())
+    return (2 * total * row + 2 * 2 * cfg.B * row + 2 * cfg.B * cfg.Hq * cfg.d * 2 + cfg.B * cfg.Hq * 4
+            + cfg.B * 4 + blocks * 4)
 
 
 def varlen_flops(cfg, q_lens, k_lens):
@@ -266,6 +282,37 @@ def main():
     vflops = varlen_flops(vcfg, vq_lens, vk_lens)
     vtflops = vflops / (var_ms * 1e-3) / 1e12
 
+    # the decode workload on a paged cache, new rows appended, timed on its own
+    del vqd, vkd, vvd, vo, vl
+    px = inputs.paged_config_inputs(dcfg, PAGED_BLOCK)
+    pqd, pknd, pvnd = px["q"].to(dev), px["k_new"].to(dev), px["v_new"].to(dev)
+    pkp, pvp = px["k_pages"].to(dev), px["v_pages"].to(dev)
+    ptbl, plens = px["block_table"].to(dev), px["seqlens"].to(dev)
+    del px
+    pmax = max_len
+    po = torch.empty_like(pqd)
+    plse = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device=dev)
+    pws = torch.empty(max(1, binding.decode_paged_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.d, pmax)),
+                      dtype=torch.uint8, device=dev)
+
+    def paged():
+        # the same rows are appended at the same positions on every call
+        binding.decode_paged(pqd, pkp, pvp, ptbl, plens, pmax, dcfg.scale, pknd, pvnd, out=po, lse=plse,
+                             workspace=pws)
+
+    for _ in range(args.warmup):
+        paged()
+    torch.cuda.synchronize()
+    pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pa.record()
+    for _ in range(K):
+        paged()
+    pb.record()
+    torch.cuda.synchronize()
+    paged_ms = pa.elapsed_time(pb) / K
+    pbytes = paged_decode_bytes(dcfg, lens, PAGED_BLOCK)
+    pgbs = pbytes / (paged_ms * 1e-3) / 1e9
+
     pre_traffic = measured_traffic("prefill")
     dec_traffic = measured_traffic("decode")
     result = {
@@ -294,6 +341,9 @@ def main():
             "varlen_prefill": {"B": vcfg.B, "Hq": vcfg.Hq, "Hkv": vcfg.Hkv, "d": vcfg.d, "causal": vcfg.causal,
                                "chunk": vcfg.chunk, "sum_q": int(vq_lens.sum()), "sum_k": int(vk_lens.sum()),
                                "max_k": vmax_k, "ms": round(var_ms, 4), "flops_per_launch": vflops},
+            "decode_paged": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d, "block_size": PAGED_BLOCK,
+                             "appended_rows": dcfg.B, "sum_len": total_len, "ms": round(paged_ms, 4),
+                             "bytes_per_launch": pbytes, "GB/s": round(pgbs, 1)},
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -304,6 +354,8 @@ def main():
         "roofline_varlen_prefill": {"bound": "mfma", "achieved": round(vtflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                                     "unit": "TFLOP/s", "frac": round(vtflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                     "traffic": None},
+        "roofline_decode_paged": {"bound": "hbm", "achieved": round(pgbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": None},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, pcfg)

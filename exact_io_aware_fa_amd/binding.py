@@ -16,7 +16,7 @@ _LIBNAME = "libfa.so"
 
 FA_F32, FA_BF16 = 0, 1
 FA_OK = 0
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 
@@ -54,6 +54,11 @@ def load_library():
     lib.fa_decode.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_paged.argtypes = [i32, p, p, p, p, p, p, p, i32, i32, i32, i32, p, p, i32, i32, i32, i32, f32,
+                                    p, sz, p]
+    lib.fa_decode_paged.restype = i32
+    lib.fa_decode_paged_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.fa_decode_paged_workspace_bytes.restype = sz
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -193,6 +198,50 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                        _dev_ptr(cu_seqlens_k), int(max_seqlen_k), _dev_ptr(out), _dev_ptr(lse),
                        B, Hq, Hkv, d, float(scale), _dev_ptr(workspace),
                        workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != FA_OK:
+        _raise(lib, st)
+    return out, lse
+
+
+def decode_paged_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_seqlen_k: int) -> int:
+    return int(load_library().fa_decode_paged_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k))
+
+
+def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 seqlens_k: torch.Tensor, max_seqlen_k: int, scale: float, k_new: torch.Tensor | None = None,
+                 v_new: torch.Tensor | None = None, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None, stream=None):
+    """Paged decode, appending the new token's rows first when k_new/v_new are given.
+    q [B,Hq,d]; caches [num_blocks,block_size,Hkv,d] (updated in place); block_table int32
+    [B,max_blocks]; seqlens_k int32 [B] (rows before the append); k_new/v_new [B,Hkv,d]
+    -> (o [B,Hq,d], lse [B,Hq] fp32)."""
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B,Hq,d] and caches [num_blocks,block_size,Hkv,d]")
+    B, Hq, d = q.shape
+    num_blocks, block_size, Hkv, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q and caches")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None and (tuple(k_new.shape) != (B, Hkv, d) or tuple(v_new.shape) != (B, Hkv, d)):
+        raise ValueError("k_new and v_new must be [B,Hkv,d]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    if seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B:
+        raise ValueError("seqlens_k must be int32 with B entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    need = int(lib.fa_decode_paged_workspace_bytes(B, Hq, Hkv, d, int(max_seqlen_k)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.fa_decode_paged(_dtype_code(q), _dev_ptr(q), _dev_ptr(k_new), _dev_ptr(v_new), _dev_ptr(k_cache),
+                             _dev_ptr(v_cache), _dev_ptr(block_table), _dev_ptr(seqlens_k), num_blocks, block_size,
+                             block_table.shape[1], int(max_seqlen_k), _dev_ptr(out), _dev_ptr(lse), B, Hq, Hkv, d,
+                             float(scale), _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream_handle(stream))
     if st != FA_OK:
         _raise(lib, st)
     return out, lse

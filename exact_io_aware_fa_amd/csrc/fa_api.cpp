@@ -229,3 +229,115 @@ FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_c
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+namespace {
+
+// Paged decode workspace: the tile prefix sums [B+1] int32 (256-byte padded),
+// then the split's partial results, planned for up to max_seqlen_k + 1 keys
+// per sequence (room for an appended row).
+struct PagedLayout {
+  DecodeLayout dec;
+  size_t part_offset;
+  size_t bytes;
+};
+
+PagedLayout paged_layout(int B, int Hq, int Hkv, int d, int max_seqlen_k) {
+  PagedLayout p{decode_layout(B, Hq, Hkv, d, max_seqlen_k + 1), 0, 0};
+  p.part_offset = ((size_t)(B + 1) * sizeof(int32_t) + 255) / 256 * 256;
+  p.bytes = p.part_offset + p.dec.bytes;
+  return p;
+}
+
+}  // namespace
+
+FA_EXPORT size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_seqlen_k < 0 || max_seqlen_k == INT_MAX || Hq % Hkv != 0)
+    return 0;
+  return paged_layout(B, Hq, Hkv, d, max_seqlen_k).bytes;
+}
+
+FA_EXPORT fa_status_t fa_decode_paged(fa_dtype_t dtype, const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* block_table,
+                                      const int32_t* seqlens_k, int num_blocks, int block_size,
+                                      int max_blocks_per_seq, int max_seqlen_k, void* o, float* lse, int B,
+                                      int Hq, int Hkv, int d, float scale, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || max_seqlen_k < 0 || num_blocks < 0 || max_blocks_per_seq < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size (B=%d max_seqlen_k=%d num_blocks=%d max_blocks_per_seq=%d)", B,
+                max_seqlen_k, num_blocks, max_blocks_per_seq);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (d <= 0) return fail(FA_ERR_INVALID_ARG, "head dim d=%d", d);
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and positive (got %g)", (double)scale);
+  if (block_size < fa::kDecodeTile || (block_size & (block_size - 1)) != 0 || block_size > (1 << 24))
+    return fail(FA_ERR_INVALID_ARG, "block_size=%d must be a power of two from %d to 2^24", block_size,
+                fa::kDecodeTile);
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(FA_ERR_INVALID_ARG, "k_new and v_new must both be given or both be null");
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "decode supports bf16 only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (Hq / Hkv > fa::decode_max_group())
+    return fail(FA_ERR_UNSUPPORTED, "Hq/Hkv=%d above %d", Hq / Hkv, fa::decode_max_group());
+  if (B == 0) return ok();
+  const int append = k_new ? 1 : 0;
+  if (max_seqlen_k == INT_MAX) return fail(FA_ERR_UNSUPPORTED, "max_seqlen_k too large");
+  if ((int64_t)max_seqlen_k + append > (int64_t)max_blocks_per_seq * block_size)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_k=%d (+%d appended) exceeds the table's %d blocks of %d rows",
+                max_seqlen_k, append, max_blocks_per_seq, block_size);
+  if ((int64_t)B * Hq > INT32_MAX || (int64_t)B * max_blocks_per_seq > ((int64_t)1 << 62) ||
+      (int64_t)B * (((int64_t)max_seqlen_k + 1 + fa::kDecodeTile - 1) / fa::kDecodeTile) > INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "B, max_blocks_per_seq or max_seqlen_k too large");
+  if (!q || !o || !lse || !block_table || !seqlens_k)
+    return fail(FA_ERR_INVALID_ARG, "null q, o, lse, block_table or seqlens_k pointer");
+  if (num_blocks > 0 && (!k_cache || !v_cache)) return fail(FA_ERR_INVALID_ARG, "null cache pointer");
+  if (max_blocks_per_seq < 1) return fail(FA_ERR_INVALID_ARG, "max_blocks_per_seq must be at least 1");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
+      !aligned16(workspace) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(FA_ERR_INVALID_ARG, "tensor and workspace pointers must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u) != 0)
+    return fail(FA_ERR_INVALID_ARG, "block_table and seqlens_k must be 4-byte aligned");
+  const size_t need = fa_decode_paged_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
+  const size_t qo_bytes = (size_t)B * Hq * d * 2;
+  const size_t lse_bytes = (size_t)B * Hq * sizeof(float);
+  const size_t new_bytes = (size_t)B * Hkv * d * 2;
+  const size_t cache_bytes = (size_t)num_blocks * block_size * Hkv * d * 2;
+  const size_t table_bytes = (size_t)B * max_blocks_per_seq * sizeof(int32_t);
+  const size_t len_bytes = (size_t)B * sizeof(int32_t);
+  // written: o, lse, workspace, and (appending) both caches; none may overlap
+  // anything else the call reads or writes
+  struct Span { const void* p; size_t n; bool written; };
+  const Span spans[] = {{q, qo_bytes, false},          {k_new, new_bytes, false},
+                        {v_new, new_bytes, false},      {block_table, table_bytes, false},
+                        {seqlens_k, len_bytes, false},  {k_cache, cache_bytes, append != 0},
+                        {v_cache, cache_bytes, append != 0}, {o, qo_bytes, true},
+                        {lse, lse_bytes, true},         {workspace, need, true}};
+  const int ns = (int)(sizeof spans / sizeof spans[0]);
+  for (int i = 0; i < ns; ++i)
+    for (int j = i + 1; j < ns; ++j)
+      if ((spans[i].written || spans[j].written) && overlaps(spans[i].p, spans[i].n, spans[j].p, spans[j].n))
+        return fail(FA_ERR_INVALID_ARG, "outputs, workspace or written caches alias other arguments");
+
+  const PagedLayout lay = paged_layout(B, Hq, Hkv, d, max_seqlen_k);
+  char* ws = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws + lay.part_offset);
+  float* part_lse = reinterpret_cast<float*>(ws + lay.part_offset + lay.dec.lse_offset);
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < block_size) ++bs_log2;
+  fa::DecodeArgs a{q, k_cache, v_cache, nullptr, o, lse, part_o, part_lse, B, Hq, Hkv, d,
+                   lay.dec.ranges, scale, reinterpret_cast<hipStream_t>(stream)};
+  a.block_table = block_table;
+  a.seqlens = seqlens_k;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cu_tiles = reinterpret_cast<int32_t*>(ws);
+  a.max_blocks = max_blocks_per_seq;
+  a.bs_log2 = bs_log2;
+  a.num_blocks = num_blocks;
+  const hipError_t e = fa::launch_decode_paged_bf16(a);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -41,13 +41,21 @@
 //    P^T of the following O^T += V^T P^T.
 //  * V^T, the A operand of that product, is read transposed from the V tile
 //    with ds_read_b64_tr_b16.
+//
+// Paged cache (PAGED): rows live in blocks of a power-of-two size >= 32 that a
+// block table maps per sequence; the new token's K/V row may be appended
+// first.  A prep kernel writes the appended rows into their blocks and the
+// prefix sums of each sequence's 32-key tiles; the split then takes whole
+// tiles as its units, so that every tile lies inside one block and its rows
+// are found with one table lookup (a scalar load) per tile.  The combine is
+// the same, over tile units.
 #include "fa_common.h"
 #include "fa_kernels.h"
 
 namespace fa {
 namespace {
 
-constexpr int kTile = 32;           // keys per tile
+constexpr int kTile = kDecodeTile;  // keys per tile
 constexpr int kGMax = 16;           // query heads per kv head (one MFMA column block)
 constexpr float kRescaleSlack = 8.0f;
 
@@ -63,6 +71,7 @@ template <int D>
 struct KvTile {
   u32x4 k[kTile * D * 2 / 1024];       // K rows, 1 KB per wave load
   u32x4 v[kTile * D * 2 / 1024];       // V rows, 1 KB per wave load
+  int nv;                              // rows of the tile that are keys of the piece (may be <= 0)
 };
 
 // ---- the even split.  bound(r) = floor(r K / R) is the first unit of range r.
@@ -96,11 +105,14 @@ __device__ __forceinline__ int sequence_of(const int32_t* __restrict__ cu, int B
 
 constexpr int kMaxHW = 8;           // kv heads (waves) per split workgroup
 
-template <int D>
+// Units: (sequence, key) pairs with cu the packed cache's offsets, or
+// (PAGED) (sequence, 32-key tile) pairs with cu the tile prefix sums.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cu, float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq,
-    int Hkv, int R, float c) {
+    int Hkv, int R, float c, const int32_t* __restrict__ table, const int32_t* __restrict__ seqlens,
+    int max_blocks, int bs_log2, int num_blocks, int append) {
   constexpr int DT = D / 32;                  // MFMA k-steps of S^T (32 head-dim values each)
   constexpr int DB = D / 16;                  // 16-wide head-dim blocks of O^T
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
@@ -155,22 +167,48 @@ __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
       ++b;
       continue;
     }
-    // ---- the piece: keys [k0, k0 + n) of (sequence b, kv head g)
+    // ---- the piece: units [k0, k0 + n) of (sequence b, kv head g), i.e.
+    // keys [k0, k0 + n), or (PAGED) the keys of tiles [k0, k0 + n), of which
+    // the first nkeys exist
     const int k0 = (int)(u - start);
     const int64_t piece_end = min(u_end, (int64_t)start + L);
     const int n = (int)(piece_end - u);
+    const int nkeys = PAGED ? min(max(seqlens[b], 0) + append - k0 * kTile, n * kTile) : n;
 
     // buffer views over the piece's rows of kv head g; rows >= n read 0
-    const int64_t row0 = ((int64_t)(start + k0) * Hkv + g) * D;
-    const uint32_t nbytes = (uint32_t)((n - 1) * Hkv + 1) * D * 2;
+    const int64_t row0 = PAGED ? 0 : ((int64_t)(start + k0) * Hkv + g) * D;
+    const uint32_t nbytes = PAGED ? 0u : (uint32_t)((n - 1) * Hkv + 1) * D * 2;
     const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kc + row0, nbytes);
     const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(vc + row0, nbytes);
     auto load_tile = [&](KvTile<D>& t, const int tile) {
-      const uint32_t base = (uint32_t)tile * kTile * rstride + ld_lane;
+      if constexpr (!PAGED) {
+        t.nv = n - tile * kTile;
+        const uint32_t base = (uint32_t)tile * kTile * rstride + ld_lane;
 #pragma unroll
-      for (int i = 0; i < VL; ++i) t.k[i] = buffer_load16(k_rsrc, base + i * RPL * rstride);
+        for (int i = 0; i < VL; ++i) t.k[i] = buffer_load16(k_rsrc, base + i * RPL * rstride);
 #pragma unroll
-      for (int i = 0; i < VL; ++i) t.v[i] = buffer_load16(v_rsrc, base + i * RPL * rstride);
+        for (int i = 0; i < VL; ++i) t.v[i] = buffer_load16(v_rsrc, base + i * RPL * rstride);
+      } else {
+        // the tile's rows: one block, found by one (scalar) table lookup; a
+        // tile past the piece, past the table's row or with an entry outside
+        // [0, num_blocks) is empty (its view has no bytes, so it reads 0)
+        const int key0 = (k0 + tile) * kTile;
+        const int blk = key0 >> bs_log2;
+        int nv = min(nkeys - tile * kTile, kTile);
+        const bool in_table = nv > 0 && blk < max_blocks;
+        const int pb = table[in_table ? (int64_t)b * max_blocks + blk : 0];
+        const bool ok = in_table && pb >= 0 && pb < num_blocks;
+        nv = ok ? nv : 0;
+        t.nv = nv;
+        const int64_t prow = ok ? ((int64_t)pb << bs_log2) + (key0 & ((1 << bs_log2) - 1)) : 0;
+        const uint32_t tbytes = nv > 0 ? (uint32_t)((nv - 1) * Hkv + 1) * D * 2 : 0u;
+        const __amdgpu_buffer_rsrc_t kr = make_rsrc(kc + (prow * Hkv + g) * D, tbytes);
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(vc + (prow * Hkv + g) * D, tbytes);
+#pragma unroll
+        for (int i = 0; i < VL; ++i) t.k[i] = buffer_load16(kr, ld_lane + i * RPL * rstride);
+#pragma unroll
+        for (int i = 0; i < VL; ++i) t.v[i] = buffer_load16(vr, ld_lane + i * RPL * rstride);
+      }
       // issue these loads before any of the following compute (the scheduler
       // would otherwise hoist the previous tile's first wait above them)
       __builtin_amdgcn_sched_barrier(0);
@@ -221,7 +259,7 @@ __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
         }
       }
       // mask keys past the piece's end, then the online softmax of head l16
-      const int thr = n - 1 - (tile * kTile + 4 * grp);
+      const int thr = t.nv - 1 - 4 * grp;
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -268,7 +306,7 @@ __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
     // the loads and computes are unconditional so that the only waits are for
     // the tile about to be used (a load issued on one path only would make the
     // compiler wait for every load at the join).
-    const int ntiles = (n + kTile - 1) / kTile;
+    const int ntiles = PAGED ? n : (n + kTile - 1) / kTile;
     KvTile<D> ta, tb;
     load_tile(ta, 0);
     for (int t = 0; t < ntiles; t += 2) {
@@ -285,7 +323,9 @@ __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
     l_rnd += __shfl_xor(l_rnd, 32, 64);
     if (l16 < G) {
       const int64_t slot = (piece_slot(k0 == 0, r, R, b) * Hkv + g) * G + l16;
-      const float inv = 1.0f / l_rnd;
+      // (a piece without keys -- possible only in a paged cache whose table
+      // points outside it -- writes O = 0 and LSE = -inf, weight 0 in the merge)
+      const float inv = l_rnd > 0.0f ? 1.0f / l_rnd : 0.0f;
       float* dst = part_o + slot * D + 4 * grp;
       // lane (head l16, group grp) item r of block db holds head-dim 16db + 4grp + r
 #pragma unroll
@@ -378,8 +418,65 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     wt += s_w[i] * sc;
     out = fmaf(s_acc[i][dd], sc, out);
   }
-  o[(int64_t)bh * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(out / wt));
-  if (dd == 0) lse[bh] = Mt + fast_log2(wt) * kLn2;
+  // (no piece with a key: O = 0, LSE = -inf, as for an empty sequence)
+  o[(int64_t)bh * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(wt > 0.0f ? out / wt : 0.0f));
+  if (dd == 0) lse[bh] = wt > 0.0f ? Mt + fast_log2(wt) * kLn2 : -INFINITY;
+}
+
+// Paged-cache preparation.  Workgroup 0 writes cu_tiles[b] = the tiles of
+// sequences 0..b-1, a sequence of L rows (L + append after the append) having
+// ceil(L / 32); workgroup 1 + b appends sequence b's new K and V rows at its
+// logical row seqlens[b] (skipped when that row lies past the table's row or
+// in a block outside [0, num_blocks)).
+constexpr int kPrepThreads = 256;
+
+__device__ __forceinline__ int tiles_of(int32_t L, int append) {
+  return (int)(((int64_t)max(L, 0) + append + kTile - 1) / kTile);
+}
+
+template <int D>
+__global__ __launch_bounds__(kPrepThreads) void paged_prep_kernel(
+    const int32_t* __restrict__ seqlens, int32_t* __restrict__ cu_tiles, const int32_t* __restrict__ table,
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ kc,
+    uint16_t* __restrict__ vc, int B, int Hkv, int max_blocks, int bs_log2, int num_blocks, int append) {
+  const int tid = threadIdx.x;
+  if (blockIdx.x == 0) {
+    // thread t sums a contiguous run of sequences; an exclusive scan of the
+    // runs' sums (in LDS) gives each run its starting offset
+    __shared__ int32_t part[kPrepThreads];
+    const int per = (B + kPrepThreads - 1) / kPrepThreads;
+    const int lo = min(B, tid * per), hi = min(B, lo + per);
+    int32_t sum = 0;
+    for (int i = lo; i < hi; ++i) sum += tiles_of(seqlens[i], append);
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kPrepThreads; off <<= 1) {
+      const int32_t x = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += x;
+      __syncthreads();
+    }
+    int32_t run = tid > 0 ? part[tid - 1] : 0;
+    for (int i = lo; i < hi; ++i) {
+      run += tiles_of(seqlens[i], append);
+      cu_tiles[i + 1] = run;
+    }
+    if (tid == 0) cu_tiles[0] = 0;
+    return;
+  }
+  const int b = blockIdx.x - 1;
+  const int L = seqlens[b];
+  if (L < 0) return;
+  const int blk = L >> bs_log2;
+  if (blk >= max_blocks) return;
+  const int pb = table[(int64_t)b * max_blocks + blk];
+  if (pb < 0 || pb >= num_blocks) return;
+  const int64_t row = ((int64_t)pb << bs_log2) + (L & ((1 << bs_log2) - 1));
+  const int chunks = Hkv * D / 8;                      // 16-byte chunks of one row
+  for (int i = tid; i < chunks; i += kPrepThreads) {
+    store16(kc + row * Hkv * D + i * 8, load16(k_new + (int64_t)b * Hkv * D + i * 8));
+    store16(vc + row * Hkv * D + i * 8, load16(v_new + (int64_t)b * Hkv * D + i * 8));
+  }
 }
 
 // Waves (kv heads) per split workgroup: the largest divisor of Hkv up to kMaxHW.
@@ -389,26 +486,45 @@ int heads_per_group(int Hkv) {
   return 1;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a) {
+  const int32_t* cu = a.cu;
+  const int append = a.k_new ? 1 : 0;
+  if (PAGED) {
+    const int64_t grid = 1 + (append ? (int64_t)a.B : 0);
+    hipLaunchKernelGGL((paged_prep_kernel<D>), dim3((unsigned)grid), dim3(kPrepThreads), 0, a.stream, a.seqlens,
+                       a.cu_tiles, a.block_table, (const uint16_t*)a.k_new, (const uint16_t*)a.v_new,
+                       (uint16_t*)const_cast<void*>(a.k_cache), (uint16_t*)const_cast<void*>(a.v_cache), a.B,
+                       a.Hkv, a.max_blocks, a.bs_log2, a.num_blocks, append);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    cu = a.cu_tiles;
+  }
   if (a.ranges > 0) {
     const int hw = heads_per_group(a.Hkv);
     const int64_t grid = (int64_t)a.ranges * (a.Hkv / hw);
     const size_t lds = (size_t)hw * 2 * kTile * D * 2;
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)grid), dim3(64 * hw), lds, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.cu,
-                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, a.ranges, a.scale * kLog2e);
+    hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)grid), dim3(64 * hw), lds, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, cu,
+                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, a.ranges, a.scale * kLog2e, a.block_table,
+                       a.seqlens, a.max_blocks, a.bs_log2, a.num_blocks, append);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(kCombineThreads), 0,
-                     a.stream, a.part_o, a.part_lse, a.cu, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.ranges);
+                     a.stream, a.part_o, a.part_lse, cu, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.ranges);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a) { return a.d == 64 ? launch<64>(a) : launch<128>(a); }
+hipError_t launch_decode_bf16(const DecodeArgs& a) {
+  return a.d == 64 ? launch<64, false>(a) : launch<128, false>(a);
+}
+
+hipError_t launch_decode_paged_bf16(const DecodeArgs& a) {
+  return a.d == 64 ? launch<64, true>(a) : launch<128, true>(a);
+}
 
 int decode_max_group() { return kGMax; }
 

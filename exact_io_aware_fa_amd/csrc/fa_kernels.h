@@ -37,12 +37,25 @@ struct DecodeArgs {
   int ranges;         // key ranges of the split (0: no keys to attend)
   float scale;
   hipStream_t stream;
+  // paged cache (launch_decode_paged_bf16 only): k_cache/v_cache are
+  // [num_blocks, 1 << bs_log2, Hkv, d]; sequence b has seqlens[b] cached rows,
+  // row i in block block_table[b * max_blocks + (i >> bs_log2)]; when k_new is
+  // set its rows [B, Hkv, d] (and v_new's) are appended first.  cu is then the
+  // workspace array [B+1] that receives the prefix sums of 32-key tiles.
+  const int32_t* block_table = nullptr;
+  const int32_t* seqlens = nullptr;
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
+  int32_t* cu_tiles = nullptr;
+  int max_blocks = 0, bs_log2 = 0, num_blocks = 0;
 };
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
 hipError_t launch_prefill_f32(const PrefillArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
+hipError_t launch_decode_paged_bf16(const DecodeArgs& a);
 
 int decode_max_group();       // largest Hq/Hkv the decode kernel handles
+constexpr int kDecodeTile = 32;   // keys per decode tile (paged blocks hold whole tiles)
 
 }  // namespace fa

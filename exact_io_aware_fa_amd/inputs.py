@@ -183,3 +183,56 @@ def varlen_config_inputs(cfg: VarlenConfig, seed: int = 0):
     k_lens = ctx + cfg.chunk
     q, k, v, cu_q, cu_k = varlen_inputs(q_lens, k_lens, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, g=g)
     return q, k, v, cu_q, cu_k, q_lens, k_lens
+
+
+def paged_decode_inputs(lens, Hq: int, Hkv: int, d: int, block_size: int, dtype: torch.dtype = torch.bfloat16,
+                        seed: int = 0, g: torch.Generator | None = None, spare_blocks: int = 3,
+                        fill: float = float("nan")):
+    """A decode step on a paged KV cache with one new row per sequence.
+
+    Draws, in order: Q, the packed caches K and V (as ``decode_inputs``), the
+    new rows k_new and v_new [B,Hkv,d], and a random order of the physical
+    blocks.  Sequence b gets ceil((L_b + 1) / block_size) blocks (room for the
+    new row), taken in that random order; its logical row i sits in row
+    i % block_size of block block_table[b, i // block_size].  Page rows that
+    hold no cached row are ``fill`` (NaN by default, so that a read of one
+    shows in the result).  Returns a dict with the packed view (q, kc, vc, cu),
+    the new rows, the pages k_pages/v_pages [num_blocks, block_size, Hkv, d],
+    block_table int32 [B, max_blocks] (unused entries -1) and seqlens int32 [B].
+    """
+    if g is None:
+        g = torch.Generator().manual_seed(seed)
+    lens = torch.as_tensor(lens, dtype=torch.int64)
+    q, kc, vc, cu = decode_inputs(lens, Hq, Hkv, d, dtype, g=g)
+    B = lens.numel()
+    k_new = _normal(g, (B, Hkv, d), dtype)
+    v_new = _normal(g, (B, Hkv, d), dtype)
+    need = [(int(L) + 1 + block_size - 1) // block_size for L in lens.tolist()]
+    num_blocks = sum(need) + spare_blocks
+    order = torch.randperm(num_blocks, generator=g)
+    max_blocks = max(need) + 1 if need else 1
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    k_pages = torch.full((num_blocks, block_size, Hkv, d), fill, dtype=dtype)
+    v_pages = torch.full((num_blocks, block_size, Hkv, d), fill, dtype=dtype)
+    nxt = 0
+    for b in range(B):
+        L, s = int(lens[b]), int(cu[b])
+        for i in range(need[b]):
+            pb = int(order[nxt])
+            nxt += 1
+            table[b, i] = pb
+            r0, r1 = i * block_size, min(L, (i + 1) * block_size)
+            if r1 > r0:
+                k_pages[pb, :r1 - r0] = kc[s + r0:s + r1]
+                v_pages[pb, :r1 - r0] = vc[s + r0:s + r1]
+    return {"q": q, "kc": kc, "vc": vc, "cu": cu, "k_new": k_new, "v_new": v_new, "k_pages": k_pages,
+            "v_pages": v_pages, "block_table": table, "seqlens": lens.to(torch.int32)}
+
+
+def paged_config_inputs(cfg: DecodeConfig, block_size: int, seed: int = 0, fill: float = 0.0):
+    """The decode workload on a paged cache: the same lengths, Q, K and V as
+    ``decode_config_inputs`` (drawn first, in that order), then the new rows
+    and the block order."""
+    g = torch.Generator().manual_seed(seed)
+    lens = decode_lengths(cfg.B, cfg.len_lo, cfg.len_hi, g)
+    return paged_decode_inputs(lens, cfg.Hq, cfg.Hkv, cfg.d, block_size, cfg.dtype, g=g, fill=fill)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
     FA_OK = 0,
@@ -163,6 +163,58 @@ fa_status_t fa_decode(fa_dtype_t dtype,
 
 /* Bytes of workspace fa_decode needs for these sizes (0 when no work). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k);
+
+/* Decode on a paged KV cache, with the new token's K/V row appended first.
+ *
+ * Each sequence's cache grows by one row per generated token, and the token
+ * attends to every row of its sequence's cache (ai6s.net page, section "what
+ * ops-transformer adds", third item).  This call does both steps: when k_new
+ * and v_new are given, the new token's key and value rows of sequence b are
+ * written into the cache as its logical row L_b = seqlens_k[b], and the
+ * token's query then attends to the L_b + 1 rows 0..L_b; when both are null
+ * it attends to the L_b cached rows only.  Per (b, query head h, kv head
+ * g = h / (Hq/Hkv)): O[b,h,:] and LSE[b,h] as in fa_decode.
+ *
+ * Layouts (all contiguous, bf16 unless noted):
+ *   q                [B, Hq, d]
+ *   k_new, v_new     [B, Hkv, d]   the new token's rows, or both NULL
+ *   k_cache, v_cache [num_blocks, block_size, Hkv, d]: logical row i of
+ *                    sequence b is row i % block_size of physical block
+ *                    block_table[b * max_blocks_per_seq + i / block_size]
+ *   block_table      int32 [B, max_blocks_per_seq], device memory
+ *   seqlens_k        int32 [B], device memory: cached rows before the append
+ *   o                [B, Hq, d];  lse  fp32 [B, Hq]
+ * block_size is a power of two from 32 to 2^24; any number of blocks and any
+ * cache size (no 4 GiB limit: every block is addressed on its own).
+ *
+ * Preconditions on device data (not checked, since that needs a sync):
+ * 0 <= seqlens_k[b] <= max_seqlen_k; the table entries of the blocks holding
+ * rows 0..L_b (0..L_b - 1 without an append) lie in [0, num_blocks); no two
+ * sequences append into the same block row.  The kernels stay inside the
+ * cache when an entry breaks this: rows in such a block are neither read nor
+ * written, and they count as absent keys (a sequence left with no key gets
+ * O = 0 and LSE = -inf).
+ *
+ * The cache is updated in place; the caller advances seqlens_k afterwards.
+ * Ownership and errors as for fa_decode; the appended rows are written before
+ * any row is read, in stream order.  The workspace holds
+ * fa_decode_paged_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k) bytes.  Returns
+ * FA_ERR_INVALID_ARG when max_seqlen_k (+1 with an append) exceeds
+ * max_blocks_per_seq * block_size, or when a written buffer (o, lse, the
+ * workspace, the caches when appending) overlaps any other argument.
+ */
+fa_status_t fa_decode_paged(fa_dtype_t dtype,
+                            const void *q, const void *k_new, const void *v_new,
+                            void *k_cache, void *v_cache,
+                            const int32_t *block_table, const int32_t *seqlens_k,
+                            int num_blocks, int block_size, int max_blocks_per_seq, int max_seqlen_k,
+                            void *o, float *lse,
+                            int B, int Hq, int Hkv, int d, float scale,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fa_decode_paged needs (0 when B is 0); the same size
+ * serves calls with and without an append. */
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k);
 
 /* Static, human-readable name of a status code. */
 const char *fa_status_str(fa_status_t status);

@@ -225,3 +225,38 @@ def decode(q, k_cache, v_cache, cu_seqlens, scale: float, nthreads: int = 0, lib
     rows = np.stack([bb.ravel(), hh.ravel()], axis=1)
     o, lse = decode_rows(q, k_cache, v_cache, cu_seqlens, scale, rows, nthreads, lib)
     return o.reshape(B, Hq, d), lse.reshape(B, Hq)
+
+
+def decode_append(q, k_cache, v_cache, cu_seqlens, k_new, v_new, scale: float, nthreads: int = 0, lib=None,
+                  rows=None):
+    """Decode after appending each sequence's new key/value row to its cache.
+
+    The new token's key and value become row L_b of sequence b, after its L_b
+    cached rows, and the token attends to all L_b + 1 rows (ai6s.net page,
+    section "what ops-transformer adds", third item: the cache grows by one row
+    per generated token and attention reads the cache's real length).  q
+    [B,Hq,d]; k_cache/v_cache [total,Hkv,d] packed by cu_seqlens (host or
+    device, int [B+1]); k_new/v_new [B,Hkv,d].  Returns (o [B,Hq,d], lse
+    [B,Hq], k_after, v_after, cu_after): the decode result in float64 and the
+    packed caches after the append (torch tensors of the caches' dtype).  With
+    ``rows`` ((b, h) pairs, as for ``decode_rows``) o and lse are [R,d] and
+    [R] for those pairs only.
+    """
+    cu = [int(x) for x in torch.as_tensor(cu_seqlens).cpu().tolist()]
+    B = len(cu) - 1
+    if k_new.shape[0] != B or v_new.shape != k_new.shape or k_new.shape[1:] != k_cache.shape[1:]:
+        raise ValueError("k_new and v_new must be [B,Hkv,d] matching the caches")
+    ks, vs, lens = [], [], []
+    for b in range(B):
+        ks += [k_cache[cu[b]:cu[b + 1]], k_new[b:b + 1]]
+        vs += [v_cache[cu[b]:cu[b + 1]], v_new[b:b + 1]]
+        lens.append(cu[b + 1] - cu[b] + 1)
+    k_after = torch.cat(ks) if ks else k_cache[:0]
+    v_after = torch.cat(vs) if vs else v_cache[:0]
+    cu_after = torch.zeros(B + 1, dtype=torch.int32)
+    cu_after[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int64), 0).to(torch.int32)
+    if rows is None:
+        o, lse = decode(q, k_after, v_after, cu_after, scale, nthreads, lib)
+    else:
+        o, lse = decode_rows(q, k_after, v_after, cu_after, scale, rows, nthreads, lib)
+    return o, lse, k_after, v_after, cu_after

@@ -32,8 +32,8 @@ def _no_gpu():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_workspace_bytes", "fa_status_str",
-              "fa_last_error", "fa_abi_version"):
+    for n in ("fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_paged",
+              "fa_decode_paged_workspace_bytes", "fa_status_str", "fa_last_error", "fa_abi_version"):
         assert n in names
 
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(fa_lib):
 
 
 def test_abi_version_and_status_names(fa_lib):
-    assert fa_lib.fa_abi_version() == 2
+    assert fa_lib.fa_abi_version() == 3
     names = [fa_lib.fa_status_str(s).decode() for s in range(5)]
     assert names == ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
                      "FA_ERR_HIP"]
@@ -180,3 +180,61 @@ def test_binding_refuses_cpu_tensors(fa_lib):
     q = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         binding.fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous(), False, 0.125)
+
+
+def _paged(lib, dtype=BF16, q=None, kn=None, vn=None, kc=None, vc=None, table=None, lens=None, num_blocks=8,
+           block_size=64, max_blocks=4, max_len=200, o=None, lse=None, B=2, Hq=8, Hkv=2, d=128, scale=0.1, ws=None,
+           ws_bytes=0):
+    return lib.fa_decode_paged(dtype, q, kn, vn, kc, vc, table, lens, num_blocks, block_size, max_blocks, max_len,
+                               o, lse, B, Hq, Hkv, d, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=F32), FA_ERR_UNSUPPORTED),
+    (dict(dtype=4), FA_ERR_INVALID_ARG),
+    (dict(B=-1), FA_ERR_INVALID_ARG),
+    (dict(max_len=-1), FA_ERR_INVALID_ARG),
+    (dict(num_blocks=-1), FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), FA_ERR_INVALID_ARG),
+    (dict(Hq=64, Hkv=2), FA_ERR_UNSUPPORTED),           # group of 32 query heads
+    (dict(d=32), FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), FA_ERR_INVALID_ARG),
+    (dict(block_size=16), FA_ERR_INVALID_ARG),          # below one 32-key tile
+    (dict(block_size=96), FA_ERR_INVALID_ARG),          # not a power of two
+    (dict(kn=0x1000), FA_ERR_INVALID_ARG),              # k_new without v_new
+    (dict(max_len=257), FA_ERR_INVALID_ARG),            # 4 blocks of 64 rows hold 256
+    (dict(), FA_ERR_INVALID_ARG),                       # null pointers
+    (dict(B=0), FA_OK),
+])
+def test_decode_paged_validation(fa_lib, kwargs, status):
+    assert _paged(fa_lib, **kwargs) == status
+    if status != FA_OK:
+        assert fa_lib.fa_last_error().decode() != ""
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device addresses; CPU-only check")
+def test_decode_paged_capacity_alignment_aliasing_and_workspace(fa_lib):
+    need = fa_lib.fa_decode_paged_workspace_bytes(2, 8, 2, 128, 200)
+    assert need > fa_lib.fa_decode_workspace_bytes(2, 8, 2, 128, 201)
+    q, kn, vn, kc, vc = 0x100000, 0x200000, 0x300000, 0x1000000, 0x2000000
+    table, lens, o, lse, ws = 0x400000, 0x500000, 0x600000, 0x700000, 0x800000
+    call = lambda **kw: _paged(fa_lib, **{**dict(q=q, kn=kn, vn=vn, kc=kc, vc=vc, table=table, lens=lens, o=o,
+                                                 lse=lse, ws=ws, ws_bytes=need), **kw})
+    # exactly full with the append: 4 blocks of 64 rows hold 255 cached rows + 1
+    assert call(max_len=256) == FA_ERR_INVALID_ARG and "exceeds" in fa_lib.fa_last_error().decode()
+    # without it 256 rows fit: the call gets past the capacity check to the workspace check
+    assert call(max_len=256, kn=None, vn=None, ws_bytes=0) == FA_ERR_WORKSPACE
+    assert call(table=table + 2) == FA_ERR_INVALID_ARG and "4-byte" in fa_lib.fa_last_error().decode()
+    assert call(kn=kn + 8) == FA_ERR_INVALID_ARG and "aligned" in fa_lib.fa_last_error().decode()
+    assert call(o=q) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
+    assert call(ws=kc + 64) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
+    assert call(vc=kc + 1024) == FA_ERR_INVALID_ARG                # the two written caches overlap
+    assert call(ws_bytes=need - 1) == FA_ERR_WORKSPACE
+    assert call(ws=None) == FA_ERR_WORKSPACE
+
+
+def test_decode_paged_workspace_size_query(fa_lib):
+    f = fa_lib.fa_decode_paged_workspace_bytes
+    assert f(0, 64, 8, 128, 1000) == 0
+    assert f(32, 64, 8, 128, 0) > 0                      # the appended row alone is work
+    assert 0 < f(32, 64, 8, 128, 512) <= f(32, 64, 8, 128, 32768)

@@ -363,6 +363,81 @@ def test_decode_matches_torch_sdpa_and_ignores_other_sequences():
         assert np.array_equal(o[b], o2[b]) and np.array_equal(lse[b], lse2[b])
 
 
+def _new_rows(B, Hkv, d, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return _randn(g, B, Hkv, d).to(dtype), _randn(g, B, Hkv, d).to(dtype)
+
+
+def test_decode_append_brute_force_tiny():
+    """Each token attends to its cached rows plus its own new row, checked by the
+    scalar brute force; an empty cache leaves only the new row."""
+    lens = [0, 1, 5, 3]
+    Hq, Hkv, d, scale = 4, 2, 8, 0.3
+    q, kc, vc, cu = inputs.decode_inputs(lens, Hq, Hkv, d, torch.float64, seed=11)
+    kn, vn = _new_rows(len(lens), Hkv, d, torch.float64, 12)
+    o, lse, ka, va, cua = oracle.decode_append(q, kc, vc, cu, kn, vn, scale)
+    for b, L in enumerate(lens):
+        s = int(cu[b])
+        keys = torch.cat([kc[s:s + L], kn[b:b + 1]])
+        vals = torch.cat([vc[s:s + L], vn[b:b + 1]])
+        bo, bl = brute.attention([[q[b].tolist()]], [keys.tolist()], [vals.tolist()], False, scale)
+        _close(o[b], np.array(bo[0][0]), 1e-12)
+        _close(lse[b], np.array([bl[0][h][0] for h in range(Hq)]), 1e-12)
+    # the caches after the append: each sequence's rows, then its new row
+    assert [int(x) for x in cua] == [0, 1, 3, 9, 13]
+    assert torch.equal(ka[cua[1] - 1], kn[0]) and torch.equal(va[cua[3] - 1], vn[2])
+    assert torch.equal(ka[cua[2]:cua[3] - 1], kc[cu[2]:cu[3]])
+
+
+def test_decode_append_to_empty_cache_returns_new_value_exactly():
+    """A single visible key: O = v_new exactly and LSE = scale * q . k_new."""
+    q, kc, vc, cu = inputs.decode_inputs([0, 0], 2, 1, 16, torch.float64, seed=13)
+    kn, vn = _new_rows(2, 1, 16, torch.float64, 14)
+    o, lse, _, _, _ = oracle.decode_append(q, kc, vc, cu, kn, vn, 0.25)
+    for b in range(2):
+        for h in range(2):
+            assert np.array_equal(o[b, h], vn[b, 0].numpy())
+            assert abs(lse[b, h] - 0.25 * math.fsum((q[b, h] * kn[b, 0]).tolist())) <= 1e-13
+
+
+def test_decode_append_merges_with_the_cached_result():
+    """Appending one key merges the cached result with the new row by the
+    logsumexp identity: LSE' = log(exp(LSE) + exp(s)), O' = w O + (1 - w) v_new
+    with w = exp(LSE - LSE'), s = scale * q . k_new (two oracle calls related
+    by the rescaling identity the online softmax rests on)."""
+    lens = [6, 40, 1]
+    Hq, Hkv, d, scale = 8, 2, 32, 0.17
+    q, kc, vc, cu = inputs.decode_inputs(lens, Hq, Hkv, d, torch.float64, seed=15)
+    kn, vn = _new_rows(3, Hkv, d, torch.float64, 16)
+    o0, l0 = oracle.decode(q, kc, vc, cu, scale)
+    o1, l1, _, _, _ = oracle.decode_append(q, kc, vc, cu, kn, vn, scale)
+    G = Hq // Hkv
+    for b in range(3):
+        for h in range(Hq):
+            s = scale * math.fsum((q[b, h] * kn[b, h // G]).tolist())
+            lse_new = max(l0[b, h], s) + math.log1p(math.exp(-abs(l0[b, h] - s)))
+            w = math.exp(l0[b, h] - lse_new)
+            assert abs(l1[b, h] - lse_new) <= 1e-12
+            _close(o1[b, h], w * o0[b, h] + (1 - w) * vn[b, h // G].numpy(), 1e-12)
+
+
+def test_decode_append_dominant_new_key_selects_new_value():
+    """A new key whose score exceeds every cached one by far more than the fp64
+    range takes all the weight: O = v_new, whichever cached rows precede it."""
+    lens = [9, 2]
+    q, kc, vc, cu = inputs.decode_inputs(lens, 2, 1, 4, torch.float64, seed=17)
+    q[:, :, :] = torch.tensor([1.0, 0.0, 0.0, 0.0], dtype=torch.float64)
+    kc[:, :, 0] = 0.0                                    # cached scores are 0
+    kn = torch.zeros(2, 1, 4, dtype=torch.float64)
+    kn[:, 0, 0] = 2000.0                                 # new score 2000 * scale
+    _, vn = _new_rows(2, 1, 4, torch.float64, 18)
+    o, lse, _, _, _ = oracle.decode_append(q, kc, vc, cu, kn, vn, 1.0)
+    for b in range(2):
+        for h in range(2):
+            assert np.array_equal(o[b, h], vn[b, 0].numpy())
+            assert lse[b, h] == 2000.0
+
+
 # ----------------------------------------------------------- input handling
 
 def test_bf16_inputs_are_widened_exactly():

@@ -356,6 +356,125 @@ def test_decode_matches_single_query_prefill():
         assert (lse[b] - lp[0, :, 0]).abs().max() <= 1e-3
 
 
+# --------------------------------------------- paged cache, new row appended
+
+def gpu_decode_paged(x, scale, append=True, table=None):
+    """Runs fa_decode_paged on the dict of ``inputs.paged_decode_inputs``;
+    returns (o, lse, k_pages after, v_pages after) on the CPU."""
+    kp, vp = x["k_pages"].cuda(), x["v_pages"].cuda()
+    tbl = (x["block_table"] if table is None else table).cuda()
+    kn = x["k_new"].cuda() if append else None
+    vn = x["v_new"].cuda() if append else None
+    max_len = int(x["seqlens"].max()) if x["seqlens"].numel() else 0
+    o, lse = binding.decode_paged(x["q"].cuda(), kp, vp, tbl, x["seqlens"].cuda(), max_len, scale, kn, vn)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu(), kp.cpu(), vp.cpu()
+
+
+def _bits(t):
+    return t.view(torch.int16)
+
+
+def expected_pages(x, append=True):
+    """The pages after the call: unchanged, plus (appending) each sequence's new
+    row at logical row L_b of its table (layout only, no arithmetic)."""
+    kp, vp = x["k_pages"].clone(), x["v_pages"].clone()
+    if append:
+        bs = kp.shape[1]
+        for b, L in enumerate(x["seqlens"].tolist()):
+            pb = int(x["block_table"][b, L // bs])
+            kp[pb, L % bs] = x["k_new"][b]
+            vp[pb, L % bs] = x["v_new"][b]
+    return kp, vp
+
+
+PAGED_CASES = [
+    # (lens, Hq, Hkv, d, block_size): empty caches, one row, tile and block edges
+    ([0, 1, 31, 32, 33, 63, 64, 65, 1000, 0], 64, 8, 128, 32),
+    ([0, 1, 31, 32, 33, 63, 64, 65, 1000, 3000], 32, 4, 64, 64),
+    ([255, 256, 257, 2049], 16, 2, 128, 256),
+    ([5, 4100], 4, 4, 128, 1024),
+]
+
+
+@pytest.mark.parametrize("append", [True, False], ids=["append", "no_append"])
+@pytest.mark.parametrize("case", PAGED_CASES, ids=lambda c: "Hq%dHkv%dd%dbs%d" % c[1:])
+def test_paged_decode(case, append):
+    """O and LSE against the oracle over the L_b (+1 appended) rows; the pages
+    afterwards hold exactly the expected rows, bit for bit, including the NaN
+    fill of unused rows (none of which may be read)."""
+    lens, Hq, Hkv, d, bs = case
+    _say("case: paged decode lens=%s Hq=%d Hkv=%d d=%d block_size=%d append=%s" % (lens, Hq, Hkv, d, bs, append))
+    x = inputs.paged_decode_inputs(lens, Hq, Hkv, d, bs, torch.bfloat16, seed=sum(lens) % 97 + d)
+    scale = inputs.fp32_scale(d)
+    o, lse, kp, vp = gpu_decode_paged(x, scale, append)
+    if append:
+        ro, rl, _, _, _ = oracle.decode_append(x["q"], x["kc"], x["vc"], x["cu"], x["k_new"], x["v_new"], scale)
+    else:
+        ro, rl = oracle.decode(x["q"], x["kc"], x["vc"], x["cu"], scale)
+    assert_close(o, ro, 1e-2, "O")
+    assert_close(lse, rl, 1e-3, "LSE")
+    ek, ev = expected_pages(x, append)
+    assert torch.equal(_bits(kp), _bits(ek)) and torch.equal(_bits(vp), _bits(ev))
+
+
+def test_paged_decode_other_sequences_have_no_effect_bitwise():
+    lens = [900, 1500, 700]
+    x = inputs.paged_decode_inputs(lens, 64, 8, 128, 64, torch.bfloat16, seed=21)
+    o1, l1, _, _ = gpu_decode_paged(x, inputs.fp32_scale(128))
+    y = dict(x)
+    y["k_pages"], y["v_pages"] = x["k_pages"].clone(), x["v_pages"].clone()
+    g = torch.Generator().manual_seed(2)
+    for pb in x["block_table"][1].tolist():
+        if pb >= 0:
+            y["k_pages"][pb] = (torch.randn(y["k_pages"][pb].shape, generator=g) * 2).to(torch.bfloat16)
+            y["v_pages"][pb] = (torch.randn(y["v_pages"][pb].shape, generator=g) * 2).to(torch.bfloat16)
+    o2, l2, _, _ = gpu_decode_paged(y, inputs.fp32_scale(128))
+    for b in (0, 2):
+        assert torch.equal(o1[b], o2[b]) and torch.equal(l1[b], l2[b])
+    assert not torch.equal(o1[1], o2[1])
+
+
+def test_paged_decode_entry_outside_the_cache_is_an_absent_block():
+    """A block-table entry outside [0, num_blocks) breaks the precondition; its
+    block is then neither read nor written and its rows count as absent keys."""
+    lens = [200, 300]
+    bs = 64
+    x = inputs.paged_decode_inputs(lens, 16, 2, 128, bs, torch.bfloat16, seed=22)
+    table = x["block_table"].clone()
+    nb = x["k_pages"].shape[0]
+    table[1, 1] = nb + 5                                  # rows 64..127 of sequence 1
+    o, lse, kp, vp = gpu_decode_paged(x, inputs.fp32_scale(128), table=table)
+    keep = [i for i in range(lens[1]) if not bs <= i < 2 * bs]
+    s1 = int(x["cu"][1])
+    kc = torch.cat([x["kc"][:s1], x["kc"][s1:][keep]])
+    vc = torch.cat([x["vc"][:s1], x["vc"][s1:][keep]])
+    cu = inputs.cu_from_lengths([lens[0], len(keep)])
+    ro, rl, _, _, _ = oracle.decode_append(x["q"], kc, vc, cu, x["k_new"], x["v_new"], inputs.fp32_scale(128))
+    assert_close(o, ro, 1e-2, "O")
+    assert_close(lse, rl, 1e-3, "LSE")
+    ek, ev = expected_pages(x, True)
+    assert torch.equal(_bits(kp), _bits(ek)) and torch.equal(_bits(vp), _bits(ev))
+
+
+def test_paged_decode_workload_full_size_sampled():
+    """The decode workload's lengths, Q, K and V on a paged cache of 64-row
+    blocks, one new row appended per sequence; sampled heads against the oracle,
+    and every page row checked after the append."""
+    cfg = inputs.DECODE_VARLEN_BF16
+    _say("case: %s, paged (64-row blocks), new row appended (sampled heads)" % cfg.name)
+    x = inputs.paged_config_inputs(cfg, 64, fill=float("nan"))
+    o, lse, kp, vp = gpu_decode_paged(x, cfg.scale)
+    rows = np.array([(b, h) for b in range(cfg.B) for h in (0, 9, 63)])
+    ro, rl, _, _, _ = oracle.decode_append(x["q"], x["kc"], x["vc"], x["cu"], x["k_new"], x["v_new"], cfg.scale,
+                                           rows=rows)
+    assert_close(o[rows[:, 0], rows[:, 1]], ro, 1e-2, "O (sampled)")
+    assert_close(lse[rows[:, 0], rows[:, 1]], rl, 1e-3, "LSE (sampled)")
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    ek, ev = expected_pages(x, True)
+    assert torch.equal(_bits(kp), _bits(ek)) and torch.equal(_bits(vp), _bits(ev))
+
+
 # ------------------------------------------------- variable-length / chunked prefill
 
 def gpu_fwd_varlen(q, k, v, cu_q, cu_k, max_q, max_k, causal, scale):

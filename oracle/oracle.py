@@ -5,10 +5,13 @@ the CPU-baseline leg of ``bench.py`` may import this module.  The GPU path
 (``exact_io_aware_fa_amd``) never imports it, and this module imports nothing
 from that package.
 
-The arithmetic lives in ``oracle.c`` (plain C, fp64, the textbook definition of
-attention: S = scale*Q K^T, mask, softmax, P V, LSE = m + ln l).  This file only
-marshals arrays: it passes the stored bit patterns of the inputs (f64, f32 or
-bf16) to C, which widens them exactly.
+The forward arithmetic lives in ``oracle.c`` (plain C, fp64, the textbook
+definition of attention: S = scale*Q K^T, mask, softmax, P V, LSE = m + ln l);
+this file passes the stored bit patterns of the inputs (f64, f32 or bf16) to C,
+which widens them exactly.  The compositions here (varlen prefill, decode after
+an append) only slice and concatenate inputs around those calls.  The backward
+(``attention_bwd``) is the chain rule of the same definition in float64 numpy,
+with library matrix products.
 
 Sources: ai6s.net page, sections "standard attention's fatal flaw is data
 movement, not compute" and "FlashAttention changes the dataflow, not the
@@ -260,3 +263,69 @@ def decode_append(q, k_cache, v_cache, cu_seqlens, k_new, v_new, scale: float, n
     else:
         o, lse = decode_rows(q, k_after, v_after, cu_after, scale, rows, nthreads, lib)
     return o, lse, k_after, v_after, cu_after
+
+
+def _f64(t) -> np.ndarray:
+    """Exact float64 copy of a float64, float32 or bfloat16 tensor (bf16 and
+    fp32 values are exactly representable in fp64)."""
+    return torch.as_tensor(t).detach().cpu().to(torch.float64).numpy()
+
+
+def attention_bwd(q, k, v, do, causal: bool, scale: float, kv_heads=None, with_magnitudes: bool = False):
+    """Gradients of exact attention for a loss L with dL/dO = do.
+
+    The pages give no backward algorithm (the training speed-ups on the
+    effectstory.com page and the ai6s.net page's section "the data" rest on
+    one); this is the derivative of the plain definition that the forward
+    oracle computes (ai6s.net page, section "standard attention's fatal flaw is
+    data movement, not compute": S = scale Q K^T, P = softmax(S) over the
+    visible keys, O = P V), by the chain rule:
+        dV = P^T dO,   dP = dO V^T,
+        dS_ij = P_ij (dP_ij - sum_l P_il dP_il)       (the softmax Jacobian),
+        dQ = scale dS K,   dK = scale dS^T Q,
+    with the mask of the forward (bottom-right causal) and GQA heads summed
+    into their kv head (kv head = h / (Hq/Hkv)).  A row with no visible key has
+    P = 0 and contributes nothing.  Library matrix products in float64.
+
+    q, do [B,N,Hq,d]; k, v [B,Nk,Hkv,d].  Returns (dq [B,N,Hq,d], dk, dv
+    [B,Nk,Hkv,d]) in float64; with ``kv_heads`` (a list of kv heads) only those
+    heads' dk, dv and their query heads' dq are computed (the rest are 0).
+    With ``with_magnitudes`` it also returns (mq, mk, mv): the same sums with
+    every term replaced by its absolute value (scale |dS| |K|, scale |dS|^T |Q|,
+    P^T |dO|), which bound the effect of rounding each term.
+    """
+    Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, N, Hq, d = Q.shape
+    Nk, Hkv = K.shape[1], K.shape[2]
+    if Hq % Hkv or dO.shape != Q.shape or V.shape != K.shape:
+        raise ValueError("shape mismatch")
+    G = Hq // Hkv
+    dq, dk, dv = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    mq, mk, mv = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    visible = np.ones((N, Nk), dtype=bool)
+    if causal:
+        visible = np.arange(Nk)[None, :] <= np.arange(N)[:, None] + (Nk - N)
+    for b in range(B):
+        for g in (range(Hkv) if kv_heads is None else kv_heads):
+            Kg, Vg = K[b, :, g, :], V[b, :, g, :]
+            for h in range(g * G, (g + 1) * G):
+                Qh, dOh = Q[b, :, h, :], dO[b, :, h, :]
+                S = np.where(visible, scale * (Qh @ Kg.T), -np.inf)
+                m = S.max(axis=1, keepdims=True)
+                m = np.where(np.isfinite(m), m, 0.0)
+                E = np.exp(S - m)                       # 0 where masked
+                l = E.sum(axis=1, keepdims=True)
+                P = np.divide(E, l, out=np.zeros_like(E), where=l > 0)
+                dP = dOh @ Vg.T
+                dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+                dv[b, :, g, :] += P.T @ dOh
+                dq[b, :, h, :] = scale * (dS @ Kg)
+                dk[b, :, g, :] += scale * (dS.T @ Qh)
+                if with_magnitudes:
+                    aS = np.abs(dS)
+                    mv[b, :, g, :] += P.T @ np.abs(dOh)
+                    mq[b, :, h, :] = scale * (aS @ np.abs(Kg))
+                    mk[b, :, g, :] += scale * (aS.T @ np.abs(Qh))
+    if with_magnitudes:
+        return dq, dk, dv, (mq, mk, mv)
+    return dq, dk, dv

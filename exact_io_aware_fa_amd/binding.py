@@ -16,7 +16,7 @@ _LIBNAME = "libfa.so"
 
 FA_F32, FA_BF16 = 0, 1
 FA_OK = 0
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lib = None
 
@@ -59,6 +59,10 @@ def load_library():
     lib.fa_decode_paged.restype = i32
     lib.fa_decode_paged_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_decode_paged_workspace_bytes.restype = sz
+    lib.fa_bwd.argtypes = [i32, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, f32, p, sz, p]
+    lib.fa_bwd.restype = i32
+    lib.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_status_str.argtypes = [i32]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -245,3 +249,34 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     if st != FA_OK:
         _raise(lib, st)
     return out, lse
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+        causal: bool, scale: float, dq: torch.Tensor | None = None, dk: torch.Tensor | None = None,
+        dv: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    """Backward of ``fwd``: q, o, dout [B,N,Hq,d], k, v [B,Nk,Hkv,d] (bf16), lse [B,Hq,N] fp32
+    -> (dq, dk, dv) in the layouts of q, k, v."""
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D BSHD tensors")
+    B, N, Hq, d = q.shape
+    Bk, Nk, Hkv, dk_ = k.shape
+    if Bk != B or dk_ != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 [B, Hq, N]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = int(lib.fa_bwd_workspace_bytes(B, Hq, N))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(_dtype_code(q), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
+                    _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), B, Hq, Hkv, N, Nk, d,
+                    1 if causal else 0, float(scale), _dev_ptr(workspace),
+                    workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if st != FA_OK:
+        _raise(lib, st)
+    return dq, dk, dv

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HIP_SOURCES = ["fa_prefill_bf16.hip", "fa_prefill_f32.hip", "fa_decode.hip"]
+HIP_SOURCES = ["fa_prefill_bf16.hip", "fa_prefill_f32.hip", "fa_decode.hip", "fa_bwd_bf16.hip"]
 HOST_SOURCES = ["fa_api.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-I", INCLUDE, "-I", CSRC,

@@ -341,3 +341,61 @@ FA_EXPORT fa_status_t fa_decode_paged(fa_dtype_t dtype, const void* q, const voi
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
+
+FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  // D then the base-2 LSE, [B, Hq, N] fp32 each, the second 256-byte aligned
+  const size_t one = ((size_t)B * Hq * N * sizeof(float) + 255) / 256 * 256;
+  return 2 * one;
+}
+
+FA_EXPORT fa_status_t fa_bwd(fa_dtype_t dtype, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int Hq,
+                             int Hkv, int N, int Nk, int d, int causal, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (B < 0 || N < 0 || Nk < 0) return fail(FA_ERR_INVALID_ARG, "negative size (B=%d N=%d Nk=%d)", B, N, Nk);
+  if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (d <= 0) return fail(FA_ERR_INVALID_ARG, "head dim d=%d", d);
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(FA_ERR_INVALID_ARG, "scale must be finite and positive (got %g)", (double)scale);
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "the backward supports bf16 only");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (B == 0 || (N == 0 && Nk == 0)) return ok();
+  if ((int64_t)B * N > INT32_MAX || (int64_t)B * Nk > INT32_MAX ||
+      (int64_t)B * Hq * ((N + 63) / 64) > INT32_MAX - 8 || (int64_t)B * Hkv * ((Nk + 63) / 64) > INT32_MAX - 8 ||
+      (int64_t)B * N * Hq * (d / 8) > ((int64_t)1 << 40))
+    return fail(FA_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+  if (((int64_t)N + 256) * Hq * d * 2 >= INT32_MAX || ((int64_t)Nk + 256) * Hkv * d * 2 >= INT32_MAX)
+    return fail(FA_ERR_UNSUPPORTED, "one batch of q or k/v exceeds 2 GiB");
+  if (N > 0 && (!q || !o || !lse || !dout || !dq)) return fail(FA_ERR_INVALID_ARG, "null q, o, lse, dout or dq pointer");
+  if (Nk > 0 && (!k || !v || !dk || !dv)) return fail(FA_ERR_INVALID_ARG, "null k, v, dk or dv pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return fail(FA_ERR_INVALID_ARG, "tensor and workspace pointers must be 16-byte aligned");
+  const size_t need = fa_bwd_workspace_bytes(B, Hq, N);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
+  const size_t q_bytes = (size_t)B * N * Hq * d * 2;
+  const size_t kv_bytes = (size_t)B * Nk * Hkv * d * 2;
+  const size_t lse_bytes = (size_t)B * Hq * N * sizeof(float);
+  struct Span { const void* p; size_t n; bool written; };
+  const Span spans[] = {{q, q_bytes, false},   {k, kv_bytes, false},  {v, kv_bytes, false},
+                        {o, q_bytes, false},   {lse, lse_bytes, false}, {dout, q_bytes, false},
+                        {dq, q_bytes, true},   {dk, kv_bytes, true},  {dv, kv_bytes, true},
+                        {workspace, need, true}};
+  const int ns = (int)(sizeof spans / sizeof spans[0]);
+  for (int i = 0; i < ns; ++i)
+    for (int j = i + 1; j < ns; ++j)
+      if ((spans[i].written || spans[j].written) && overlaps(spans[i].p, spans[i].n, spans[j].p, spans[j].n))
+        return fail(FA_ERR_INVALID_ARG, "gradients or workspace alias other arguments");
+
+  float* dsum = static_cast<float*>(workspace);
+  float* lse2 = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, dsum, lse2, B, Hq, Hkv, N, Nk, d, causal != 0, scale,
+                reinterpret_cast<hipStream_t>(stream)};
+  const hipError_t e = fa::launch_bwd_bf16(a);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

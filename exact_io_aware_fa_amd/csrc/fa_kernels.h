@@ -50,7 +50,28 @@ struct DecodeArgs {
   int max_blocks = 0, bs_log2 = 0, num_blocks = 0;
 };
 
+// Backward (bf16): dq [B,N,Hq,d], dk/dv [B,Nk,Hkv,d] from q, k, v, o, dout and
+// the forward's lse [B,Hq,N]; dsum and lse2 are workspace arrays [B,Hq,N].
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;
+  float* lse2;
+  int B, Hq, Hkv, N, Nk, d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a);
+hipError_t launch_bwd_bf16(const BwdArgs& a);
 hipError_t launch_prefill_f32(const PrefillArgs& a);
 hipError_t launch_decode_bf16(const DecodeArgs& a);
 hipError_t launch_decode_paged_bf16(const DecodeArgs& a);

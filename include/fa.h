@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
     FA_OK = 0,
@@ -215,6 +215,36 @@ fa_status_t fa_decode_paged(fa_dtype_t dtype,
 /* Bytes of workspace fa_decode_paged needs (0 when B is 0); the same size
  * serves calls with and without an append. */
 size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k);
+
+/* Backward of fa_fwd: gradients dq, dk, dv of a loss whose gradient with
+ * respect to O is dout (bf16).
+ *
+ * The pages state no backward algorithm; this is the chain rule of the
+ * forward's definition (ai6s.net page, section "standard attention's fatal
+ * flaw is data movement, not compute"), with P recomputed from the forward's
+ * LSE (P_ij = exp(scale q_i.k_j - LSE_i) over the visible keys):
+ *   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D) with D_i = dO_i . O_i,
+ *   dQ = scale dS K,  dK = scale dS^T Q;
+ * the same mask as fa_fwd (bottom-right when causal), and for grouped heads
+ * dk, dv of kv head g sum over query heads g*(Hq/Hkv) .. (g+1)*(Hq/Hkv)-1.
+ *
+ * Layouts (contiguous BSHD, bf16): q, o, dout, dq [B, N, Hq, d]; k, v, dk, dv
+ * [B, Nk, Hkv, d]; lse [B, Hq, N] fp32 as written by fa_fwd for the same
+ * q, k, v, causal and scale (o as well: D uses it).  Rows without a visible
+ * key (LSE = -inf) get dq = 0 and add nothing to dk, dv.
+ * Workspace: fa_bwd_workspace_bytes(B, Hq, N) bytes, caller-owned.
+ * Ownership, asynchrony and errors as for fa_fwd; FA_ERR_UNSUPPORTED for
+ * fp32 or d not in {64, 128}; FA_ERR_INVALID_ARG when a gradient or the
+ * workspace overlaps another argument.  Deterministic: no atomics.
+ */
+fa_status_t fa_bwd(fa_dtype_t dtype,
+                   const void *q, const void *k, const void *v, const void *o, const float *lse,
+                   const void *dout, void *dq, void *dk, void *dv,
+                   int B, int Hq, int Hkv, int N, int Nk, int d, int causal, float scale,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace fa_bwd needs (0 when there are no query rows). */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N);
 
 /* Static, human-readable name of a status code. */
 const char *fa_status_str(fa_status_t status);

@@ -292,7 +292,10 @@ def attention_bwd(q, k, v, do, causal: bool, scale: float, kv_heads=None, with_m
     heads' dk, dv and their query heads' dq are computed (the rest are 0).
     With ``with_magnitudes`` it also returns (mq, mk, mv): the same sums with
     every term replaced by its absolute value (scale |dS| |K|, scale |dS|^T |Q|,
-    P^T |dO|), which bound the effect of rounding each term.
+    P^T |dO|), plus, for dq and dk, the terms through which the row constant
+    D_i = sum_l P_il dP_il enters dS (scale a_i P |K| and scale P^T (a |Q|),
+    a_i = sum_d |dO_id O_id|); they bound the effect of rounding each term,
+    and of computing D from a rounded O.
     """
     Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(do)
     B, N, Hq, d = Q.shape
@@ -323,9 +326,10 @@ def attention_bwd(q, k, v, do, causal: bool, scale: float, kv_heads=None, with_m
                 dk[b, :, g, :] += scale * (dS.T @ Qh)
                 if with_magnitudes:
                     aS = np.abs(dS)
+                    a = np.abs(dOh * (P @ Vg)).sum(axis=1, keepdims=True)     # [N, 1]
                     mv[b, :, g, :] += P.T @ np.abs(dOh)
-                    mq[b, :, h, :] = scale * (aS @ np.abs(Kg))
-                    mk[b, :, g, :] += scale * (aS.T @ np.abs(Qh))
+                    mq[b, :, h, :] = scale * ((aS + a * P) @ np.abs(Kg))
+                    mk[b, :, g, :] += scale * ((aS + a * P).T @ np.abs(Qh))
     if with_magnitudes:
         return dq, dk, dv, (mq, mk, mv)
     return dq, dk, dv

@@ -33,7 +33,8 @@ def _no_gpu():
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_paged",
-              "fa_decode_paged_workspace_bytes", "fa_status_str", "fa_last_error", "fa_abi_version"):
+              "fa_decode_paged_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str",
+              "fa_last_error", "fa_abi_version"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(fa_lib):
 
 
 def test_abi_version_and_status_names(fa_lib):
-    assert fa_lib.fa_abi_version() == 3
+    assert fa_lib.fa_abi_version() == 4
     names = [fa_lib.fa_status_str(s).decode() for s in range(5)]
     assert names == ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
                      "FA_ERR_HIP"]
@@ -238,3 +239,40 @@ def test_decode_paged_workspace_size_query(fa_lib):
     assert f(0, 64, 8, 128, 1000) == 0
     assert f(32, 64, 8, 128, 0) > 0                      # the appended row alone is work
     assert 0 < f(32, 64, 8, 128, 512) <= f(32, 64, 8, 128, 32768)
+
+
+def _bwd(lib, dtype=BF16, p=None, B=1, Hq=4, Hkv=2, N=64, Nk=64, d=128, causal=1, scale=0.1, ws=None,
+         ws_bytes=0):
+    return lib.fa_bwd(dtype, p, p, p, p, p, p, p, p, p, B, Hq, Hkv, N, Nk, d, causal, scale, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=F32), FA_ERR_UNSUPPORTED),
+    (dict(dtype=9), FA_ERR_INVALID_ARG),
+    (dict(B=-1), FA_ERR_INVALID_ARG),
+    (dict(N=-1), FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), FA_ERR_INVALID_ARG),
+    (dict(d=96), FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), FA_ERR_INVALID_ARG),
+    (dict(), FA_ERR_INVALID_ARG),                       # null pointers
+    (dict(B=0), FA_OK),
+    (dict(N=0, Nk=0), FA_OK),
+])
+def test_bwd_validation(fa_lib, kwargs, status):
+    assert _bwd(fa_lib, **kwargs) == status
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="uses fake device addresses; CPU-only check")
+def test_bwd_alignment_aliasing_and_workspace(fa_lib):
+    need = fa_lib.fa_bwd_workspace_bytes(1, 4, 64)
+    assert need >= 2 * 4 * 64 * 4 and fa_lib.fa_bwd_workspace_bytes(1, 4, 0) == 0
+    base = [0x100000 * (i + 1) for i in range(10)]
+    q, k, v, o, lse, do, dq, dk, dv, ws = base
+    call = lambda **kw: fa_lib.fa_bwd(BF16, *[kw.get(n, x) for n, x in zip(
+        ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"), (q, k, v, o, lse, do, dq, dk, dv))],
+        1, 4, 2, 64, 64, 128, 1, 0.1, kw.get("ws", ws), kw.get("ws_bytes", need), None)
+    assert call(dq=dq + 4) == FA_ERR_INVALID_ARG and "aligned" in fa_lib.fa_last_error().decode()
+    assert call(dq=q) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
+    assert call(dk=dv) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
+    assert call(ws=do) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
+    assert call(ws_bytes=need - 1) == FA_ERR_WORKSPACE

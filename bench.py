@@ -20,11 +20,17 @@ per visible (query, key) pair.  Then the decode workload on a paged cache of
 64-row blocks, with each sequence's new K/V row appended in the same call
 (fa_decode_paged), is timed and reported as `roofline_decode_paged` in GB/s of
 algorithmic bytes (the cached rows, the new rows read and written, q, o, lse,
-the lengths and the block-table entries used, each once).
+the lengths and the block-table entries used, each once).  Last, the backward
+of the prefill workload (fa_bwd, given the forward's O and LSE and a seeded
+dO) is timed and reported as `roofline_backward`, counting the five products
+of the chain rule (S recomputed, dP, dV, dK, dQ: 2.5 times the forward's
+flops); the kernels compute S and dP twice (seven products), which the count
+leaves out.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --pmc-pass      # one launch of each kernel plus a copy of known
-                                    # size, for rocprofv3 counter collection
+    python bench.py --pmc-pass      # a copy of known size, then one launch of each part
+                                    # (prefill, decode, paged decode, backward), for
+                                    # rocprofv3 counter collection
     python bench.py --traffic-summary FETCH.csv WRITE.csv
                                     # counters of two such passes -> profiles/traffic.json
 """
@@ -48,9 +54,19 @@ _CSRC = "exact_io_aware_fa_amd/csrc/"
 TRAFFIC_SOURCES = {
     "prefill": [_CSRC + "fa_prefill_bf16.hip", _CSRC + "fa_common.h"],
     "decode": [_CSRC + "fa_decode.hip", _CSRC + "fa_common.h", _CSRC + "fa_api.cpp"],
+    "decode_paged": [_CSRC + "fa_decode.hip", _CSRC + "fa_common.h", _CSRC + "fa_api.cpp"],
+    "backward": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h"],
 }
-# kernel-name fragments of each part (decode = split + combine)
-TRAFFIC_KERNELS = {"prefill": ["prefill_bf16_kernel"], "decode": ["decode_split_kernel", "decode_combine_kernel"]}
+# Kernels of each part: the kernel-name fragment of the part's first launch,
+# and the fragments of all its kernels.  The counter pass launches the parts
+# one after the other, so a dispatch belongs to the last part started before
+# it (the paged decode reuses the decode's kernel names).
+TRAFFIC_KERNELS = {
+    "prefill": ("prefill_bf16_kernel", ["prefill_bf16_kernel"]),
+    "decode": ("decode_split_kernel<128, false>", ["decode_split_kernel", "decode_combine_kernel"]),
+    "decode_paged": ("paged_prep_kernel", ["paged_prep_kernel", "decode_split_kernel", "decode_combine_kernel"]),
+    "backward": ("bwd_pre_kernel", ["bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]),
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PMC_COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 
@@ -74,16 +90,30 @@ def measured_traffic(part):
 
 
 def _counter_per_dispatch(csv_path, counter):
-    """{dispatch id: (kernel name, value summed over the counter's instances)}"""
+    """{dispatch id (int): (kernel name, value summed over the counter's instances)}"""
     import csv
     out = {}
     with open(csv_path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            name, val = out.get(r["Dispatch_Id"], (r["Kernel_Name"], 0.0))
-            out[r["Dispatch_Id"]] = (name, val + float(r["Counter_Value"]))
+            did = int(r["Dispatch_Id"])
+            name, val = out.get(did, (r["Kernel_Name"], 0.0))
+            out[did] = (name, val + float(r["Counter_Value"]))
     return out
+
+
+def _part_of_dispatches(disp):
+    """{dispatch id: part} following the launch order of the counter pass."""
+    parts, cur = {}, None
+    for did in sorted(disp):
+        name = disp[did][0]
+        for part, (start, _) in TRAFFIC_KERNELS.items():
+            if start in name:
+                cur = part
+        if cur is not None and any(fr in name for fr in TRAFFIC_KERNELS[cur][1]):
+            parts[did] = cur
+    return parts
 
 
 def traffic_summary(fetch_csv, write_csv):
@@ -101,9 +131,10 @@ def traffic_summary(fetch_csv, write_csv):
         copies = [v for n, v in disp.values() if "copyBuffer" in n]
         factor = PMC_COPY_BYTES / (max(copies) * 1024.0)
         factors[counter] = factor
-        for part, frags in TRAFFIC_KERNELS.items():
-            per_part[part][counter] = sum(v * 1024.0 * factor for n, v in disp.values()
-                                          if any(fr in n for fr in frags))
+        owner = _part_of_dispatches(disp)
+        for part in TRAFFIC_KERNELS:
+            per_part[part][counter] = sum(v * 1024.0 * factor for did, (n, v) in disp.items()
+                                          if owner.get(did) == part)
     for part, c in per_part.items():
         result[part] = {"fetch_bytes_per_launch": round(c["FETCH_SIZE"]),
                         "write_bytes_per_launch": round(c["WRITE_SIZE"]),
@@ -169,6 +200,39 @@ def cpu_baseline(q, k, v, cfg):
                       "%.1f s wall" % (len(rows), cfg.Hq, dt)}
 
 
+def setup_paged(torch, binding, inputs, dcfg, dev, max_len):
+    """The decode workload on a paged cache of PAGED_BLOCK-row blocks with the
+    new rows appended: returns the launch closure."""
+    px = inputs.paged_config_inputs(dcfg, PAGED_BLOCK)
+    t = {n: px[n].to(dev) for n in ("q", "k_new", "v_new", "k_pages", "v_pages", "block_table", "seqlens")}
+    del px
+    t["o"] = torch.empty_like(t["q"])
+    t["lse"] = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device=dev)
+    t["ws"] = torch.empty(max(1, binding.decode_paged_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.d, max_len)),
+                          dtype=torch.uint8, device=dev)
+
+    def paged():
+        # the same rows are appended at the same positions on every call
+        binding.decode_paged(t["q"], t["k_pages"], t["v_pages"], t["block_table"], t["seqlens"], max_len,
+                             dcfg.scale, t["k_new"], t["v_new"], out=t["o"], lse=t["lse"], workspace=t["ws"])
+    return paged
+
+
+def setup_backward(torch, binding, pcfg, dev, qd, kd, vd, o, lse):
+    """The backward of the prefill workload for a seeded dO (o and lse must
+    hold the forward's results): returns the launch closure."""
+    g = torch.Generator().manual_seed(1)
+    gdo = torch.randn(tuple(qd.shape), generator=g, dtype=torch.float32).to(torch.bfloat16).to(dev)
+    grads = (torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd))
+    gws = torch.empty(max(1, int(binding.load_library().fa_bwd_workspace_bytes(pcfg.B, pcfg.Hq, pcfg.N))),
+                      dtype=torch.uint8, device=dev)
+
+    def backward():
+        binding.bwd(qd, kd, vd, o, lse, gdo, pcfg.causal, pcfg.scale, dq=grads[0], dk=grads[1], dv=grads[2],
+                    workspace=gws)
+    return backward
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,9 +284,14 @@ def main():
         src = torch.empty(PMC_COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
+        paged = setup_paged(torch, binding, inputs, dcfg, dev, max_len)
+        backward = setup_backward(torch, binding, pcfg, dev, qd, kd, vd, o, lse)
+        torch.cuda.synchronize()
         dst.copy_(src)
         prefill()
         decode()
+        paged()
+        backward()
         torch.cuda.synchronize()
         print(json.dumps({"pmc_pass": True, "copy_bytes": PMC_COPY_BYTES}))
         return
@@ -284,22 +353,7 @@ def main():
 
     # the decode workload on a paged cache, new rows appended, timed on its own
     del vqd, vkd, vvd, vo, vl
-    px = inputs.paged_config_inputs(dcfg, PAGED_BLOCK)
-    pqd, pknd, pvnd = px["q"].to(dev), px["k_new"].to(dev), px["v_new"].to(dev)
-    pkp, pvp = px["k_pages"].to(dev), px["v_pages"].to(dev)
-    ptbl, plens = px["block_table"].to(dev), px["seqlens"].to(dev)
-    del px
-    pmax = max_len
-    po = torch.empty_like(pqd)
-    plse = torch.empty((dcfg.B, dcfg.Hq), dtype=torch.float32, device=dev)
-    pws = torch.empty(max(1, binding.decode_paged_workspace_bytes(dcfg.B, dcfg.Hq, dcfg.Hkv, dcfg.d, pmax)),
-                      dtype=torch.uint8, device=dev)
-
-    def paged():
-        # the same rows are appended at the same positions on every call
-        binding.decode_paged(pqd, pkp, pvp, ptbl, plens, pmax, dcfg.scale, pknd, pvnd, out=po, lse=plse,
-                             workspace=pws)
-
+    paged = setup_paged(torch, binding, inputs, dcfg, dev, max_len)
     for _ in range(args.warmup):
         paged()
     torch.cuda.synchronize()
@@ -313,8 +367,27 @@ def main():
     pbytes = paged_decode_bytes(dcfg, lens, PAGED_BLOCK)
     pgbs = pbytes / (paged_ms * 1e-3) / 1e9
 
+    # backward of the prefill workload, timed on its own
+    del paged
+    prefill()
+    backward = setup_backward(torch, binding, pcfg, dev, qd, kd, vd, o, lse)
+    for _ in range(args.warmup):
+        backward()
+    torch.cuda.synchronize()
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record()
+    for _ in range(K):
+        backward()
+    gb.record()
+    torch.cuda.synchronize()
+    bwd_ms = ga.elapsed_time(gb) / K
+    bflops = 2.5 * flops
+    btflops = bflops / (bwd_ms * 1e-3) / 1e12
+
     pre_traffic = measured_traffic("prefill")
     dec_traffic = measured_traffic("decode")
+    paged_traffic = measured_traffic("decode_paged")
+    bwd_traffic = measured_traffic("backward")
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -344,6 +417,8 @@ def main():
             "decode_paged": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d, "block_size": PAGED_BLOCK,
                              "appended_rows": dcfg.B, "sum_len": total_len, "ms": round(paged_ms, 4),
                              "bytes_per_launch": pbytes, "GB/s": round(pgbs, 1)},
+            "backward": {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "N": pcfg.N, "Nk": pcfg.Nk, "d": pcfg.d,
+                         "causal": pcfg.causal, "ms": round(bwd_ms, 4), "flops_per_launch": bflops},
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -355,7 +430,10 @@ def main():
                                     "unit": "TFLOP/s", "frac": round(vtflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                     "traffic": None},
         "roofline_decode_paged": {"bound": "hbm", "achieved": round(pgbs, 1), "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": None},
+                                  "unit": "GB/s", "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": paged_traffic},
+        "roofline_backward": {"bound": "mfma", "achieved": round(btflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(btflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "traffic": bwd_traffic},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, pcfg)

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * WQ) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dq, int N, int Nk, int Hq, int Hkv, float c, float scale, int n_qtiles, int n_work) {
-  static_assert(WQ * 64 == kThr, "staging copies assume 256 threads");
+  static_assert(WQ * 64 >= kThr, "staging copies use the first 256 threads");
   constexpr int DT = D / 32, DB = D / 16, CPR = D / 8;
   constexpr int ROWS_W = 16 * RB, ROWS_G = ROWS_W * WQ;
   __shared__ __attribute__((aligned(1024))) uint16_t sK[2][kT * D];
@@ -207,16 +207,19 @@ __global__ __launch_bounds__(64 * WQ) void bwd_dq_kernel(
     for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   TileCopy<D> ck, cv;
+  const bool copier = tid < kThr;
   if (n_kv > 0) {
-    ck.load(k_rsrc, 0, kv_row_bytes, tid);
-    cv.load(v_rsrc, 0, kv_row_bytes, tid);
-    ck.store(reinterpret_cast<char*>(sK[0]), tid);
-    cv.store(reinterpret_cast<char*>(sV[0]), tid);
+    if (copier) {
+      ck.load(k_rsrc, 0, kv_row_bytes, tid);
+      cv.load(v_rsrc, 0, kv_row_bytes, tid);
+      ck.store(reinterpret_cast<char*>(sK[0]), tid);
+      cv.store(reinterpret_cast<char*>(sV[0]), tid);
+    }
     __syncthreads();
   }
   for (int j = 0; j < n_kv; ++j) {
     const bool more = j + 1 < n_kv;
-    if (more) {
+    if (more && copier) {
       ck.load(k_rsrc, (j + 1) * kT, kv_row_bytes, tid);
       cv.load(v_rsrc, (j + 1) * kT, kv_row_bytes, tid);
     }
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(64 * WQ) void bwd_dq_kernel(
       for (int rb = 0; rb < RB; ++rb)
         acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dsf[rb], acc[rb][db], 0, 0, 0);
     }
-    if (more) {
+    if (more && copier) {
       // the other buffers were last read in iteration j-1, before its barrier
       ck.store(reinterpret_cast<char*>(sK[(j + 1) & 1]), tid);
       cv.store(reinterpret_cast<char*>(sV[(j + 1) & 1]), tid);
@@ -519,8 +522,20 @@ __global__ __launch_bounds__(64 * WK) void bwd_dkdv_kernel(
   }
 }
 
-constexpr int kWQ = 4, kRBQ = 2;    // bwd_dq: 4 waves x 32 rows
-constexpr int kWK = 4, kRBK = 1;    // bwd_dkdv: 4 waves x 16 keys
+#ifndef BWD_WQ
+#define BWD_WQ 4
+#endif
+#ifndef BWD_RBQ
+#define BWD_RBQ 2
+#endif
+#ifndef BWD_WK
+#define BWD_WK 8
+#endif
+#ifndef BWD_RBK
+#define BWD_RBK 1
+#endif
+constexpr int kWQ = BWD_WQ, kRBQ = BWD_RBQ;    // bwd_dq: waves x 16-row blocks per wave
+constexpr int kWK = BWD_WK, kRBK = BWD_RBK;    // bwd_dkdv: waves x 16-key blocks per wave
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {

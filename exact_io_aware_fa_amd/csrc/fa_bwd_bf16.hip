@@ -411,41 +411,48 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
 
   // staging of iteration `it`: Q and dO tiles of head g*G + it/per_head,
   // rows (qt0 + it%per_head)*32..; lse2 (+inf past N) and D for those rows
-  TileCopy<D> cq, co;
-  float stage_l = INFINITY, stage_d = 0.0f;
-  auto load_it = [&](const int it) {
+  // Two register sets of staged tiles: the loads of tile it+2 are issued at
+  // the start of iteration it (its Q and dO rows mostly come from beyond L2),
+  // and tile it+1, loaded one iteration earlier, is stored to LDS at its end.
+  struct Stage {
+    TileCopy<D> cq, co;
+    float l = INFINITY, d = 0.0f;
+  };
+  Stage st0, st1;
+  auto load_it = [&](const int it, Stage& st) {
     const int h = g * G + it / per_head;
     const int i0 = (qt0 + it % per_head) * kT;
     if (tid < kThr) {
-      cq.load(head_rsrc(q, h), i0, q_row_bytes, tid);
-      co.load(head_rsrc(dout, h), i0, q_row_bytes, tid);
+      st.cq.load(head_rsrc(q, h), i0, q_row_bytes, tid);
+      st.co.load(head_rsrc(dout, h), i0, q_row_bytes, tid);
     }
     if (tid < kT) {
       const int row = i0 + tid;
       const int64_t li = ((int64_t)b * Hq + h) * N + (row < N ? row : 0);
-      stage_l = row < N ? lse2[li] : INFINITY;
-      stage_d = row < N ? dsum[li] : 0.0f;
+      st.l = row < N ? lse2[li] : INFINITY;
+      st.d = row < N ? dsum[li] : 0.0f;
     }
   };
-  auto store_it = [&](const int buf) {
+  auto store_it = [&](const int buf, const Stage& st) {
     if (tid < kThr) {
-      cq.store(reinterpret_cast<char*>(sQ[buf]), tid);
-      co.store(reinterpret_cast<char*>(sO[buf]), tid);
+      st.cq.store(reinterpret_cast<char*>(sQ[buf]), tid);
+      st.co.store(reinterpret_cast<char*>(sO[buf]), tid);
     }
     if (tid < kT) {
-      sL[buf][tid] = stage_l;
-      sD[buf][tid] = stage_d;
+      sL[buf][tid] = st.l;
+      sD[buf][tid] = st.d;
     }
   };
 
   if (n_it > 0) {
-    load_it(0);
-    store_it(0);
+    load_it(0, st0);
+    if (n_it > 1) load_it(1, st1);
+    store_it(0, st0);
     __syncthreads();
   }
-  for (int it = 0; it < n_it; ++it) {
-    const bool more = it + 1 < n_it;
-    if (more) load_it(it + 1);
+  // iteration `it`: `ld` receives tile it+2, `nx` holds tile it+1
+  auto step = [&](const int it, Stage& ld, Stage& nx) __attribute__((always_inline)) {
+    if (it + 2 < n_it) load_it(it + 2, ld);
     const int i0 = (qt0 + it % per_head) * kT;
     const char* qt = reinterpret_cast<const char*>(sQ[it & 1]);
     const char* ot = reinterpret_cast<const char*>(sO[it & 1]);
@@ -517,8 +524,13 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
         acc_k[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, dsf[rb], acc_k[rb][db], 0, 0, 0);
       }
     }
-    if (more) store_it((it + 1) & 1);                // last read in iteration it-1, before its barrier
+    if (it + 1 < n_it) store_it((it + 1) & 1, nx);  // last read in iteration it-1, before its barrier
     __syncthreads();
+  };
+  for (int it = 0; it < n_it; it += 2) {
+    step(it, st0, st1);
+    if (it + 1 >= n_it) break;
+    step(it + 1, st1, st0);
   }
 
 #pragma unroll

@@ -93,18 +93,18 @@ __global__ __launch_bounds__(kThr) void bwd_pre_kernel(const uint16_t* __restric
   }
 }
 
-// Copies of one 32-row tile of a [rows, H, D] tensor slice into LDS: thread t
-// moves 16-byte chunks t, t + 256, ... (row = chunk / CPR).
-template <int D>
+// Copies of one 32-row tile of a [rows, H, D] tensor slice into LDS by THR
+// threads: thread t moves 16-byte chunks t, t + THR, ... (row = chunk / CPR).
+template <int D, int THR = kThr>
 struct TileCopy {
   static constexpr int CPR = D / 8;
-  static constexpr int CH = kT * CPR / kThr;      // chunks per thread (2 at d=128, 1 at d=64)
-  static_assert(CH >= 1 && kT * CPR % kThr == 0, "tile chunks spread evenly over the threads");
+  static constexpr int CH = kT * CPR / THR;       // chunks per thread
+  static_assert(CH >= 1 && kT * CPR % THR == 0, "tile chunks spread evenly over the threads");
   u32x4 r[CH];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int row0, uint32_t row_bytes, int tid) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int id = tid + kThr * i;
+      const int id = tid + THR * i;
       const int row = id / CPR, col = id % CPR;
       r[i] = buffer_load16(rsrc, (uint32_t)(row0 + row) * row_bytes + col * 16);
     }
@@ -112,7 +112,7 @@ struct TileCopy {
   __device__ __forceinline__ void store(char* tile, int tid) const {
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const int id = tid + kThr * i;
+      const int id = tid + THR * i;
       const int row = id / CPR, col = id % CPR;
       store16(tile + row * (2 * D) + ((col ^ swz<CPR>(row)) * 16), r[i]);
     }
@@ -321,6 +321,7 @@ __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
 #define BWD_OCC 1
 #endif
 
+
 // ---- dK and dV.  Workgroup: WK waves x (16 RB) keys of one kv head; it
 // streams 32-row Q and dO tiles (with their lse2 and D) of every query head
 // of the group, from the first query tile that sees one of its keys.
@@ -330,7 +331,6 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int Nk, int Hq, int Hkv, float c, float scale,
     int n_ktiles, int n_work) {
-  static_assert(WK * 64 >= kThr, "staging copies use the first 256 threads");
   constexpr int DT = D / 32, DB = D / 16, CPR = D / 8;
   constexpr int KEYS_W = 16 * RB, KEYS_G = KEYS_W * WK;
   __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][kT * D];
@@ -409,20 +409,23 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc_k[rb][db] = acc_v[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // staging of iteration `it`: Q and dO tiles of head g*G + it/per_head,
-  // rows (qt0 + it%per_head)*32..; lse2 (+inf past N) and D for those rows
-  // Two register sets of staged tiles: the loads of tile it+2 are issued at
-  // the start of iteration it (its Q and dO rows mostly come from beyond L2),
-  // and tile it+1, loaded one iteration earlier, is stored to LDS at its end.
+  // Staging of iteration `it`: Q and dO tiles of head g*G + it/per_head,
+  // rows (qt0 + it%per_head)*32..; lse2 (+inf past N) and D for those rows.
+  // Their loads mostly miss L2, so they run two tiles ahead: two register
+  // sets, tile t in set t % 2; the loads of tile it+2 are issued at the start
+  // of iteration it, and tile it+1 is stored to LDS at its end.  (A third set
+  // makes the unrolled loop spill at d=128.)  CT threads copy: one 16-byte
+  // chunk each per tensor at d=128 with 8 waves.
+  constexpr int CT = 64 * WK < kT * CPR ? 64 * WK : kT * CPR;
   struct Stage {
-    TileCopy<D> cq, co;
+    TileCopy<D, CT> cq, co;
     float l = INFINITY, d = 0.0f;
   };
   Stage st0, st1;
   auto load_it = [&](const int it, Stage& st) {
     const int h = g * G + it / per_head;
     const int i0 = (qt0 + it % per_head) * kT;
-    if (tid < kThr) {
+    if (tid < CT) {
       st.cq.load(head_rsrc(q, h), i0, q_row_bytes, tid);
       st.co.load(head_rsrc(dout, h), i0, q_row_bytes, tid);
     }
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
     }
   };
   auto store_it = [&](const int buf, const Stage& st) {
-    if (tid < kThr) {
+    if (tid < CT) {
       st.cq.store(reinterpret_cast<char*>(sQ[buf]), tid);
       st.co.store(reinterpret_cast<char*>(sO[buf]), tid);
     }

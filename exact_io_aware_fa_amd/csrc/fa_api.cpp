@@ -201,7 +201,7 @@ FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_c
   if (Hq / Hkv > fa::decode_max_group())
     return fail(FA_ERR_UNSUPPORTED, "Hq/Hkv=%d above %d", Hq / Hkv, fa::decode_max_group());
   if (B == 0) return ok();
-  if ((int64_t)B * Hq > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "B*Hq too large");
+  if (((int64_t)B + kDecodeWaves) * Hq > INT32_MAX) return fail(FA_ERR_UNSUPPORTED, "B*Hq too large");
   if (!q || !o || !lse || !cu_seqlens_k) return fail(FA_ERR_INVALID_ARG, "null q, o, lse or cu_seqlens_k pointer");
   if (max_seqlen_k > 0 && (!k_cache || !v_cache)) return fail(FA_ERR_INVALID_ARG, "null cache pointer");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) || !aligned16(lse) ||
@@ -286,7 +286,7 @@ FA_EXPORT fa_status_t fa_decode_paged(fa_dtype_t dtype, const void* q, const voi
   if ((int64_t)max_seqlen_k + append > (int64_t)max_blocks_per_seq * block_size)
     return fail(FA_ERR_INVALID_ARG, "max_seqlen_k=%d (+%d appended) exceeds the table's %d blocks of %d rows",
                 max_seqlen_k, append, max_blocks_per_seq, block_size);
-  if ((int64_t)B * Hq > INT32_MAX || (int64_t)B * max_blocks_per_seq > ((int64_t)1 << 62) ||
+  if (((int64_t)B + kDecodeWaves) * Hq > INT32_MAX || (int64_t)B * max_blocks_per_seq > ((int64_t)1 << 62) ||
       (int64_t)B * (((int64_t)max_seqlen_k + 1 + fa::kDecodeTile - 1) / fa::kDecodeTile) > INT32_MAX)
     return fail(FA_ERR_UNSUPPORTED, "B, max_blocks_per_seq or max_seqlen_k too large");
   if (!q || !o || !lse || !block_table || !seqlens_k)

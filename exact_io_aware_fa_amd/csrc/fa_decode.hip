@@ -336,34 +336,35 @@ __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
   }
 }
 
-// One workgroup per (sequence, query head): merges the pieces of its sequence:
-// the first piece, in slot R + b, and one continuation per non-empty key range
-// that starts inside the sequence, in that range's slot.  PL lanes
-// of pieces (kCombineThreads / D) each fold every PL-th piece, kBatch pieces
-// at a time with all their loads issued first; the lanes are then merged
-// through LDS.
-constexpr int kCombineThreads = 256;
-constexpr int kBatch = 16;
+// One wave per (sequence, query head), kCombineWaves per workgroup: merges the
+// pieces of its sequence -- the first piece, in slot R + b, and one
+// continuation per non-empty key range that starts inside the sequence, in
+// that range's slot -- as LSE = M + ln sum_s exp(LSE_s - M), O = sum_s
+// exp(LSE_s - LSE) O_s with M the largest LSE_s.  Lane i takes piece i of
+// each 64-piece chunk: it reads the piece's LSE (one round of loads for the
+// max, one for the weights), and then every lane folds all pieces of the
+// chunk for its D/64 head-dim values, the weight and slot of piece u read
+// from lane u.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineThreads = 64 * kCombineWaves;
 
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, const int32_t* __restrict__ cu,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int R) {
-  constexpr int PL = kCombineThreads / D;
-  __shared__ float s_m[PL], s_w[PL];
-  __shared__ float s_acc[PL][D];
-  const int bh = blockIdx.x;
-  const int b = bh / Hq, h = bh % Hq;
+  constexpr int PER = D / 64;                          // head-dim values per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t bh = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+  if (bh >= (int64_t)B * Hq) return;
+  const int b = (int)(bh / Hq), h = (int)(bh % Hq);
   const int G = Hq / Hkv;
   const int g = h / G, j = h % G;
-  const int pl = threadIdx.x / D, dd = threadIdx.x % D;
   const int start = cu[b];
   const int L = cu[b + 1] - start;
   if (L == 0 || R == 0) {                              // no keys: O = 0, LSE = -inf
-    if (pl == 0) {
-      o[(int64_t)bh * D + dd] = 0;
-      if (dd == 0) lse[bh] = -INFINITY;
-    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) o[bh * D + lane + 64 * p] = 0;
+    if (lane == 0) lse[bh] = -INFINITY;
     return;
   }
   const int64_t K = (int64_t)cu[B];
@@ -371,56 +372,62 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   const int npieces = 1 + (hi - lo);
   // a range has no units only when there are fewer units than ranges
   const bool may_be_empty = K < R;
-  // fold with a running max over the (natural-log) piece LSEs
-  float M = -INFINITY, wsum = 0.0f, acc = 0.0f;
-  for (int base = pl; base < npieces; base += PL * kBatch) {
-    float ls[kBatch], ov[kBatch];
+  auto slot_of = [&](const int i) { return (piece_slot(i == 0, lo + i, R, b) * Hkv + g) * G + j; };
+  auto present = [&](const int i) {
+    return i == 0 || !may_be_empty || part_bound(lo + i, K, R) < part_bound(lo + i + 1, K, R);
+  };
+  // the largest piece LSE (lane i holds piece i of each 64-piece chunk)
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < npieces; c0 += 64) {
+    const int i = c0 + lane;
+    if (i < npieces && present(i)) M = fmaxf(M, part_lse[slot_of(i)]);
+  }
+  M = max_xor32(max_xor16(M));
+  M = fmaxf(M, __shfl_xor(M, 8, 64));
+  M = fmaxf(M, __shfl_xor(M, 4, 64));
+  M = fmaxf(M, __shfl_xor(M, 2, 64));
+  M = fmaxf(M, __shfl_xor(M, 1, 64));
+  // each lane weighs its piece; then every lane folds the chunk's pieces for
+  // its head-dim values, reading each piece's weight and slot from its lane
+  float acc[PER] = {}, wlane_sum = 0.0f;
+  for (int c0 = 0; c0 < npieces; c0 += 64) {
+    const int i = c0 + lane;
+    const bool ok = i < npieces && present(i);
+    const int sl = ok ? (int)slot_of(i) : 0;
+    const float ls = ok ? part_lse[sl] : -INFINITY;
+    const float w = ls == -INFINITY ? 0.0f : fast_exp2((ls - M) * kLog2e);
+    wlane_sum += w;
+    const int n = min(64, npieces - c0);
+    constexpr int kU = 8;                              // pieces whose loads are in flight together
+    for (int u0 = 0; u0 < n; u0 += kU) {
+      float wv[kU], ov[kU][PER];
 #pragma unroll
-    for (int t = 0; t < kBatch; ++t) {
-      const int i = base + t * PL;
-      const int rv = lo + i;
-      // range rv >= lo+1 holds a piece of this sequence unless it has no units
-      const bool ok = i < npieces &&
-                      (i == 0 || !may_be_empty || part_bound(rv, K, R) < part_bound(rv + 1, K, R));
-      const int64_t slot = (piece_slot(i == 0, rv, R, b) * Hkv + g) * G + j;
-      ls[t] = ok ? part_lse[slot] : -INFINITY;
-      ov[t] = ok ? part_o[slot * D + dd] : 0.0f;
+      for (int u = 0; u < kU; ++u) {
+        const int src = min(u0 + u, n - 1);
+        const int su = __builtin_amdgcn_readlane(sl, src);
+        wv[u] = u0 + u < n ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), src))
+                           : 0.0f;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) ov[u][p] = part_o[(int64_t)su * D + lane + 64 * p];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int p = 0; p < PER; ++p) acc[p] = fmaf(wv[u], ov[u][p], acc[p]);
     }
-    float bm = M;
-#pragma unroll
-    for (int t = 0; t < kBatch; ++t) bm = fmaxf(bm, ls[t]);
-    if (bm == -INFINITY) continue;
-    const float sc = M == -INFINITY ? 0.0f : fast_exp2((M - bm) * kLog2e);
-    acc *= sc;
-    wsum *= sc;
-    M = bm;
-#pragma unroll
-    for (int t = 0; t < kBatch; ++t) {
-      const float wt = ls[t] == -INFINITY ? 0.0f : fast_exp2((ls[t] - M) * kLog2e);
-      wsum += wt;
-      acc = fmaf(wt, ov[t], acc);
-    }
   }
-  if (dd == 0) {
-    s_m[pl] = M;
-    s_w[pl] = wsum;
-  }
-  s_acc[pl][dd] = acc;
-  __syncthreads();
-  if (pl != 0) return;
-  float Mt = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < PL; ++i) Mt = fmaxf(Mt, s_m[i]);
-  float wt = 0.0f, out = 0.0f;
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const float sc = s_m[i] == -INFINITY ? 0.0f : fast_exp2((s_m[i] - Mt) * kLog2e);
-    wt += s_w[i] * sc;
-    out = fmaf(s_acc[i][dd], sc, out);
-  }
+  float wsum = wlane_sum;
+  wsum += __shfl_xor(wsum, 32, 64);
+  wsum += __shfl_xor(wsum, 16, 64);
+  wsum += __shfl_xor(wsum, 8, 64);
+  wsum += __shfl_xor(wsum, 4, 64);
+  wsum += __shfl_xor(wsum, 2, 64);
+  wsum += __shfl_xor(wsum, 1, 64);
   // (no piece with a key: O = 0, LSE = -inf, as for an empty sequence)
-  o[(int64_t)bh * D + dd] = __builtin_bit_cast(uint16_t, (__bf16)(wt > 0.0f ? out / wt : 0.0f));
-  if (dd == 0) lse[bh] = wt > 0.0f ? Mt + fast_log2(wt) * kLn2 : -INFINITY;
+#pragma unroll
+  for (int p = 0; p < PER; ++p)
+    o[bh * D + lane + 64 * p] = __builtin_bit_cast(uint16_t, (__bf16)(wsum > 0.0f ? acc[p] / wsum : 0.0f));
+  if (lane == 0) lse[bh] = wsum > 0.0f ? M + fast_log2(wsum) * kLn2 : -INFINITY;
 }
 
 // Paged-cache preparation.  Workgroup 0 writes cu_tiles[b] = the tiles of
@@ -511,7 +518,8 @@ hipError_t launch(const DecodeArgs& a) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)((int64_t)a.B * a.Hq)), dim3(kCombineThreads), 0,
+  const int64_t combine_blocks = ((int64_t)a.B * a.Hq + kCombineWaves - 1) / kCombineWaves;
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((unsigned)combine_blocks), dim3(kCombineThreads), 0,
                      a.stream, a.part_o, a.part_lse, cu, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.ranges);
   return hipGetLastError();
 }

@@ -320,6 +320,9 @@ __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
 #ifndef BWD_OCC
 #define BWD_OCC 1
 #endif
+#ifndef BWD_RA
+#define BWD_RA 2
+#endif
 
 
 // ---- dK and dV.  Workgroup: WK waves x (16 RB) keys of one kv head; it
@@ -477,6 +480,15 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
         }
       }
     }
+    // LDS reads run BWD_RA steps ahead of the MFMAs that use them
+    if constexpr (BWD_RA > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * BWD_RA, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
+      }
+    }
     // lse2 and D of this lane's 8 queries (8c..8c+7)
     const f32x4 la = *reinterpret_cast<const f32x4*>(&sL[it & 1][8 * grp]);
     const f32x4 lb = *reinterpret_cast<const f32x4*>(&sL[it & 1][8 * grp + 4]);
@@ -525,6 +537,14 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
       for (int rb = 0; rb < RB; ++rb) {
         acc_v[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, pf[rb], acc_v[rb][db], 0, 0, 0);
         acc_k[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, dsf[rb], acc_k[rb][db], 0, 0, 0);
+      }
+    }
+    if constexpr (BWD_RA > 0) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * BWD_RA, 0);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
       }
     }
     if (it + 1 < n_it) store_it((it + 1) & 1, nx);  // last read in iteration it-1, before its barrier

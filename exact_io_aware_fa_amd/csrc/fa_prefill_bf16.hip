@@ -425,11 +425,24 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   // stage is overwritten only after both groups have finished reading its
   // previous tile (K_{j-1}, V_{j-2}: read by the end of phase 2j-1).
   const int group = wave >= kWaves / 2 ? 1 : 0;
+  // Causal: group 0 (the first half of the tile's rows) needs only the first
+  // n0 tiles.  It runs its MFMA blocks and softmaxes for those, then, for the
+  // last n_kv - n0 tiles, only its P.V of tile n0-1 (in phase 2*n0) and the
+  // copies, so that group 1 runs those tiles without a partner on its SIMDs.
+  // Every step has two barriers, so both groups execute the same number.
+#ifndef PREFILL_EARLY_STOP
+#define PREFILL_EARLY_STOP 1
+#endif
+  int n0 = n_kv;
+  if (CAUSAL && PREFILL_EARLY_STOP) {
+    const int last_key0 = q0 + kRows * (kWaves / 2) - 1 + offs;   // group 0's last row's last key
+    n0 = max(1, min(n_kv, last_key0 < 0 ? 0 : last_key0 / kBC + 1));
+  }
   // Rounds of kNS tiles, unrolled so that every stage is named statically.
   // The check after each tile leaves the loop (it never skips ahead to the
   // next round), so at the top of a round, as far as the compiler can tell,
   // the same copies are in flight as at the end of the previous one.
-  auto run_group = [&](auto copy_tag) __attribute__((always_inline)) {
+  auto run_group = [&](auto copy_tag, const int n_end) __attribute__((always_inline)) {
     constexpr bool COPY = decltype(copy_tag)::value;
     auto step = [&](const int j, const int st) __attribute__((always_inline)) {   // j % kNS == st
       mblock(j, kS(st), vS((st + kNS - 1) % kNS), kS((st + kPD) % kNS), vS((st + kPD - 1) % kNS),
@@ -439,19 +452,19 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
       if (COPY) wait_vmem_le<(kPD - 1) * kCopiesPerBlock>();
       barrier_no_fence();
     };
-    // one round from tile j0 (< n_kv); false once the last tile is done
+    // one round from tile j0 (< n_end); false once tile n_end-1 is done
     auto round = [&](const int j0) __attribute__((always_inline)) -> bool {
       step(j0, 0);
-      if (j0 + 1 >= n_kv) return false;
+      if (j0 + 1 >= n_end) return false;
       step(j0 + 1, 1);
-      if (j0 + 2 >= n_kv) return false;
+      if (j0 + 2 >= n_end) return false;
       if constexpr (kNS > 2) {
         step(j0 + 2, 2);
-        if (j0 + 3 >= n_kv) return false;
+        if (j0 + 3 >= n_end) return false;
       }
       if constexpr (kNS > 3) {
         step(j0 + 3, 3);
-        if (j0 + 4 >= n_kv) return false;
+        if (j0 + 4 >= n_end) return false;
       }
       return true;
     };
@@ -479,14 +492,23 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     wait_vmem_all();
     barrier_no_fence();
     if (group == 0) {
-      run_group(kCopy);
+      run_group(kCopy, n0);
+      // group 0's tail (stages named at run time: no LDS reads but one P.V)
+      for (int j = n0; j < n_kv; ++j) {
+        if (j == n0) stage_pv(vS((j + kNS - 1) % kNS));   // phase 2*n0: P.V of tile n0-1
+        issue(k_slice, j + kPD, k_voff, kS((j + kPD) % kNS));
+        issue(v_slice, j + kPD - 1, v_voff, vS((j + kPD - 1) % kNS));
+        barrier_no_fence();
+        wait_vmem_le<(kPD - 1) * kCopiesPerBlock>();
+        barrier_no_fence();
+      }
       wait_vmem_all();                              // no copy may land after the workgroup ends
-      stage_pv(vS((n_kv - 1) % kNS));               // phase 2n: M_n
+      if (n0 >= n_kv) stage_pv(vS((n_kv - 1) % kNS));   // phase 2n: M_n (earlier when n0 < n_kv)
       barrier_no_fence();
       barrier_no_fence();                           // phase 2n+1: idle
     } else {
       barrier_no_fence();                           // phase 0: idle
-      run_group(kNoCopy);
+      run_group(kNoCopy, n_kv);
       stage_pv(vS((n_kv - 1) % kNS));               // phase 2n+1: M_n
       barrier_no_fence();
     }

@@ -14,10 +14,18 @@
 // gfx950 mapping
 //  * workgroup = 8 waves = 384 query rows of one (batch, query head); wave w
 //    owns rows 48w..48w+47 as three 16-row blocks.  A KV tile is 32 keys.
-//    LDS bandwidth (the reads of the MFMA operands plus the writes of the
-//    copies that fill it) is what limits this kernel: every K and V operand a
-//    wave reads feeds the MFMAs of its three row blocks, and a copied tile
-//    serves 384 rows.
+//    Every K and V operand a wave reads from LDS feeds the MFMAs of its three
+//    row blocks, and a copied tile serves 384 rows.  On this chip a wave's
+//    MFMAs and another wave's softmax (exponentials above all) barely overlap
+//    on a SIMD, so the time per tile is close to the MFMA time plus the
+//    softmax's vector time: the softmax is kept to as few vector instructions
+//    as possible.
+//  * Query tiles are aligned to the end of the sequence (a partial tile holds
+//    the first rows, which see the fewest keys) and ordered by kv head, so
+//    that with 8 kv heads each XCD holds one kv head of every sequence;
+//    causal tiles with the most keys are scheduled first.  In the diagonal
+//    band, the first half of the tile's rows stops computing after its last
+//    key tile (see the ping-pong schedule below).
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_16x16x32_bf16: K from LDS is the A operand, Q sits in
 //    registers as the B operand for the whole kernel.  The K rows of each

@@ -33,6 +33,10 @@ leaves out.
                                     # rocprofv3 counter collection
     python bench.py --traffic-summary FETCH.csv WRITE.csv
                                     # counters of two such passes -> profiles/traffic.json
+    python bench.py --mfma-summary MFMA.csv
+                                    # MFMA busy fraction and executed bf16 MFMA flops per
+                                    # part, from one pass of SQ_VALU_MFMA_BUSY_CYCLES,
+                                    # GRBM_GUI_ACTIVE and SQ_INSTS_VALU_MFMA_MOPS_BF16
 """
 import argparse
 import hashlib
@@ -68,6 +72,7 @@ TRAFFIC_KERNELS = {
     "backward": ("bwd_pre_kernel", ["bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma.json")
 PMC_COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 
 
@@ -94,6 +99,20 @@ def measured_traffic(part):
     if rec.get("sources") != {p: source_digest(p) for p in TRAFFIC_SOURCES[part]}:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def measured_mfma_flops(part):
+    """bf16 MFMA flops executed per launch of `part` (masked and recomputed
+    work included) from the committed counter summary, or None when there is
+    none or the kernel sources changed since it was taken."""
+    try:
+        with open(MFMA_FILE) as f:
+            rec = json.load(f)[part]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources") != {p: source_digest(p) for p in TRAFFIC_SOURCES[part]}:
+        return None
+    return rec.get("bf16_mfma_flops_per_launch")
 
 
 def _counter_per_dispatch(csv_path, counter):
@@ -153,6 +172,66 @@ def traffic_summary(fetch_csv, write_csv):
         json.dump(result, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(result, indent=1, sort_keys=True))
+
+
+def mfma_summary(csv_path, n_simd=1024, clock_ghz=2.4):
+    """MFMA use per part of a counter pass over `bench.py --pmc-pass`.
+
+    SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) divided by the SIMD
+    count (256 CUs x 4) is how many cycles each SIMD's matrix unit was busy;
+    over the dispatch's own duration (its trace timestamps) at the 2.4 GHz
+    peak clock that is the MFMA utilisation against the dense peak.
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 is the bf16 MFMA flops executed,
+    masked-away work included.  GRBM_GUI_ACTIVE is not used as the
+    denominator: the pass reports it summed over the XCDs and over a counter
+    window wider than the dispatch.  Writes the executed flops per launch
+    (with digests of the kernel sources) to profiles/mfma.json and prints the
+    figures."""
+    import csv
+    disp = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            did = int(r["Dispatch_Id"])
+            name = r["Kernel_Name"]
+            e = disp.setdefault(did, {"name": name, "vals": {},
+                                      "dur_s": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+            e["vals"][r["Counter_Name"]] = e["vals"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    owner = _part_of_dispatches({d: (e["name"], 0.0) for d, e in disp.items()})
+
+    def short(name):
+        name = name.split("(")[0] if "(anonymous" not in name else name.split("::")[-1]
+        return name.split("<")[0].split("(")[0].strip()
+
+    out = {"clock_ghz": clock_ghz, "n_simd": n_simd}
+    for part in TRAFFIC_KERNELS:
+        tot_busy = tot_flops = tot_dur = 0.0
+        kernels = []
+        for did, e in sorted(disp.items()):
+            if owner.get(did) != part:
+                continue
+            busy = e["vals"].get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+            flops = e["vals"].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+            tot_busy += busy
+            tot_flops += flops
+            tot_dur += e["dur_s"]
+            kernels.append({"kernel": short(e["name"]), "us": round(e["dur_s"] * 1e6, 1),
+                            "mfma_busy": round(busy / n_simd / (e["dur_s"] * clock_ghz * 1e9), 4),
+                            "bf16_mfma_flops": flops,
+                            "tflops_executed": round(flops / e["dur_s"] / 1e12, 1)})
+        out[part] = {"us": round(tot_dur * 1e6, 1), "mfma_busy_cycles": tot_busy,
+                     "mfma_busy": round(tot_busy / n_simd / max(1e-12, tot_dur * clock_ghz * 1e9), 4),
+                     "bf16_mfma_flops": tot_flops,
+                     "tflops_executed": round(tot_flops / max(1e-12, tot_dur) / 1e12, 1),
+                     "kernels": kernels}
+    rec = {part: {"bf16_mfma_flops_per_launch": out[part]["bf16_mfma_flops"],
+                  "mfma_busy_cycles_per_launch": out[part]["mfma_busy_cycles"],
+                  "sources": {p: source_digest(p) for p in TRAFFIC_SOURCES[part]}}
+           for part in TRAFFIC_KERNELS}
+    with open(MFMA_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+    return out
 
 
 def prefill_flops(cfg):
@@ -249,9 +328,14 @@ def main():
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter passes into profiles/traffic.json")
+    ap.add_argument("--mfma-summary", metavar="MFMA_CSV",
+                    help="MFMA busy fraction and bf16 MFMA flops per part from one rocprofv3 counter pass")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU; this build has no multi-GPU path "
@@ -395,6 +479,15 @@ def main():
     dec_traffic = measured_traffic("decode")
     paged_traffic = measured_traffic("decode_paged")
     bwd_traffic = measured_traffic("backward")
+
+    def mfma_use(part, ms):
+        ex = measured_mfma_flops(part)
+        if ex is None:
+            return None
+        rate = ex / (ms * 1e-3) / 1e12
+        return {"executed_flops": ex, "executed_tflops": round(rate, 1),
+                "frac": round(rate / MFMA_BF16_PEAK_TFLOPS, 4)}
+
     result = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -441,6 +534,9 @@ def main():
         "roofline_backward": {"bound": "mfma", "achieved": round(btflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(btflops / MFMA_BF16_PEAK_TFLOPS, 4),
                               "traffic": bwd_traffic},
+        "mfma_util": {"prefill": mfma_use("prefill", pre_avg), "decode": mfma_use("decode", dec_avg),
+                      "decode_paged": mfma_use("decode_paged", paged_ms),
+                      "backward": mfma_use("backward", bwd_ms)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(q, k, v, pcfg)

@@ -37,3 +37,33 @@ def test_counter_dispatches_follow_the_launch_order():
     assert 1 not in parts
     assert [parts[i] for i in range(2, 11)] == ["prefill", "decode", "decode", "decode_paged", "decode_paged",
                                                 "decode_paged", "backward", "backward", "backward"]
+
+
+def test_mfma_summary_sums_each_part(tmp_path, monkeypatch):
+    """Busy cycles over (SIMDs x duration x clock), and MOPS x 512 as flops,
+    summed over the kernels of a part; the file it writes carries digests."""
+    k = lambda s: "void fa::(anonymous namespace)::%s(int)" % s
+    rows = [(1, "__amd_rocclr_copyBuffer", 0, 1000, 0.0, 0.0),
+            (2, k("prefill_bf16_kernel<128, true, false>"), 0, 1000, 1.2e6, 2.4e6),
+            (3, k("bwd_pre_kernel<128>"), 0, 500, 0.0, 0.0),
+            (4, k("bwd_dq_kernel<128, true, 4, 2>"), 0, 1000, 0.6e6, 1.2e6),
+            (5, k("bwd_dkdv_kernel<128, true, 8, 1>"), 0, 2000, 0.6e6, 1.2e6)]
+    path = tmp_path / "c.csv"
+    with open(path, "w") as f:
+        f.write('"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"\n')
+        for did, name, t0, t1, busy, mops in rows:
+            for cn, v in (("SQ_VALU_MFMA_BUSY_CYCLES", busy), ("SQ_INSTS_VALU_MFMA_MOPS_BF16", mops),
+                          ("GRBM_GUI_ACTIVE", 1.0)):
+                f.write('%d,"%s","%s",%r,%d,%d\n' % (did, name, cn, v, t0, t1))
+    monkeypatch.setattr(bench, "MFMA_FILE", str(tmp_path / "mfma.json"))
+    out = bench.mfma_summary(str(path), n_simd=1000, clock_ghz=2.0)
+    # prefill: 1.2e6 busy cycles / 1000 SIMDs over 1 us at 2 GHz = 2000 cycles
+    assert abs(out["prefill"]["mfma_busy"] - 0.6) < 1e-9
+    assert out["prefill"]["bf16_mfma_flops"] == 2.4e6 * 512
+    # backward: 1.2e6 / 1000 over 3.5 us at 2 GHz
+    assert abs(out["backward"]["mfma_busy"] - round(1200.0 / 7000.0, 4)) < 1e-9
+    assert [x["kernel"] for x in out["backward"]["kernels"]] == ["bwd_pre_kernel", "bwd_dq_kernel",
+                                                                 "bwd_dkdv_kernel"]
+    assert out["decode"]["bf16_mfma_flops"] == 0.0
+    monkeypatch.setattr(bench, "MFMA_FILE", str(tmp_path / "mfma.json"))
+    assert bench.measured_mfma_flops("backward") == 2.4e6 * 512

@@ -57,6 +57,7 @@ _CSRC = "exact_io_aware_fa_amd/csrc/"
 # sources whose change invalidates a kernel's measured traffic
 TRAFFIC_SOURCES = {
     "prefill": [_CSRC + "fa_prefill_bf16.hip", _CSRC + "fa_common.h"],
+    "varlen_prefill": [_CSRC + "fa_prefill_bf16.hip", _CSRC + "fa_common.h"],
     "decode": [_CSRC + "fa_decode.hip", _CSRC + "fa_common.h", _CSRC + "fa_api.cpp"],
     "decode_paged": [_CSRC + "fa_decode.hip", _CSRC + "fa_common.h", _CSRC + "fa_api.cpp"],
     "backward": [_CSRC + "fa_bwd_bf16.hip", _CSRC + "fa_common.h"],
@@ -64,9 +65,11 @@ TRAFFIC_SOURCES = {
 # Kernels of each part: the kernel-name fragment of the part's first launch,
 # and the fragments of all its kernels.  The counter pass launches the parts
 # one after the other, so a dispatch belongs to the last part started before
-# it (the paged decode reuses the decode's kernel names).
+# it (the paged decode reuses the decode's kernel names; the varlen prefill's
+# name also holds the prefill's fragment, so it comes later in this table).
 TRAFFIC_KERNELS = {
     "prefill": ("prefill_bf16_kernel", ["prefill_bf16_kernel"]),
+    "varlen_prefill": ("prefill_bf16_kernel<128, true, true>", ["prefill_bf16_kernel"]),
     "decode": ("decode_split_kernel<128, false>", ["decode_split_kernel", "decode_combine_kernel"]),
     "decode_paged": ("paged_prep_kernel", ["paged_prep_kernel", "decode_split_kernel", "decode_combine_kernel"]),
     "backward": ("bwd_pre_kernel", ["bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]),
@@ -239,6 +242,15 @@ def prefill_flops(cfg):
     return f / 2 if cfg.causal else f
 
 
+def varlen_prefill_bytes(cfg, q_lens, k_lens):
+    """Algorithmic bytes of one packed varlen prefill: Q, K, V read once, O and
+    LSE written once, the two offset arrays read once."""
+    sq, sk = int(q_lens.sum()), int(k_lens.sum())
+    qo = 2 * sq * cfg.Hq * cfg.d * 2
+    kv = 2 * sk * cfg.Hkv * cfg.d * 2
+    return qo + kv + sq * cfg.Hq * 4 + 2 * (cfg.B + 1) * 4
+
+
 def decode_bytes(cfg, total_len):
     kv = 2 * total_len * cfg.Hkv * cfg.d * 2
     qo = 2 * cfg.B * cfg.Hq * cfg.d * 2
@@ -284,6 +296,24 @@ def cpu_baseline(q, k, v, cfg):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d query rows (every 8th row x %d heads) of the prefill workload, "
                       "%.1f s wall" % (len(rows), cfg.Hq, dt)}
+
+
+def setup_varlen(torch, binding, inputs, dev):
+    """The chunked varlen prefill workload resident on the device: returns
+    (launch, config, query lengths, key lengths)."""
+    vcfg = inputs.VARLEN_CHUNKED_BF16
+    vq, vk, vv, vcu_q, vcu_k, vq_lens, vk_lens = inputs.varlen_config_inputs(vcfg)
+    vqd, vkd, vvd = vq.to(dev), vk.to(dev), vv.to(dev)
+    vcuq, vcuk = vcu_q.to(dev), vcu_k.to(dev)
+    del vq, vk, vv
+    vo = torch.empty_like(vqd)
+    vl = torch.empty((vcfg.Hq, vqd.shape[0]), dtype=torch.float32, device=dev)
+    vmax_q, vmax_k = int(vq_lens.max()), int(vk_lens.max())
+
+    def varlen():
+        binding.fwd_varlen(vqd, vkd, vvd, vcuq, vcuk, vmax_q, vmax_k, vcfg.causal, vcfg.scale, out=vo, lse=vl)
+
+    return varlen, vcfg, vq_lens, vk_lens
 
 
 def setup_paged(torch, binding, inputs, dcfg, dev, max_len):
@@ -375,11 +405,13 @@ def main():
         src = torch.empty(PMC_COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
+        varlen = setup_varlen(torch, binding, inputs, dev)[0]
         paged = setup_paged(torch, binding, inputs, dcfg, dev, max_len)
         backward = setup_backward(torch, binding, pcfg, dev, qd, kd, vd, o, lse)
         torch.cuda.synchronize()
         dst.copy_(src)
         prefill()
+        varlen()
         decode()
         paged()
         backward()
@@ -417,18 +449,8 @@ def main():
     gbs = dbytes / (dec_avg * 1e-3) / 1e9
 
     # chunked variable-length prefill, timed on its own after the steps
-    vcfg = inputs.VARLEN_CHUNKED_BF16
-    vq, vk, vv, vcu_q, vcu_k, vq_lens, vk_lens = inputs.varlen_config_inputs(vcfg)
-    vqd, vkd, vvd = vq.to(dev), vk.to(dev), vv.to(dev)
-    vcuq, vcuk = vcu_q.to(dev), vcu_k.to(dev)
-    del vq, vk, vv
-    vo = torch.empty_like(vqd)
-    vl = torch.empty((vcfg.Hq, vqd.shape[0]), dtype=torch.float32, device=dev)
-    vmax_q, vmax_k = int(vq_lens.max()), int(vk_lens.max())
-
-    def varlen():
-        binding.fwd_varlen(vqd, vkd, vvd, vcuq, vcuk, vmax_q, vmax_k, vcfg.causal, vcfg.scale, out=vo, lse=vl)
-
+    varlen, vcfg, vq_lens, vk_lens = setup_varlen(torch, binding, inputs, dev)
+    vmax_k = int(vk_lens.max())
     for _ in range(args.warmup):
         varlen()
     torch.cuda.synchronize()
@@ -443,7 +465,7 @@ def main():
     vtflops = vflops / (var_ms * 1e-3) / 1e12
 
     # the decode workload on a paged cache, new rows appended, timed on its own
-    del vqd, vkd, vvd, vo, vl
+    del varlen
     paged = setup_paged(torch, binding, inputs, dcfg, dev, max_len)
     for _ in range(args.warmup):
         paged()
@@ -476,6 +498,7 @@ def main():
     btflops = bflops / (bwd_ms * 1e-3) / 1e12
 
     pre_traffic = measured_traffic("prefill")
+    var_traffic = measured_traffic("varlen_prefill")
     dec_traffic = measured_traffic("decode")
     paged_traffic = measured_traffic("decode_paged")
     bwd_traffic = measured_traffic("backward")
@@ -528,13 +551,14 @@ def main():
                             "traffic": dec_traffic},
         "roofline_varlen_prefill": {"bound": "mfma", "achieved": round(vtflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                                     "unit": "TFLOP/s", "frac": round(vtflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                                    "traffic": None},
+                                    "traffic": var_traffic},
         "roofline_decode_paged": {"bound": "hbm", "achieved": round(pgbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(pgbs / HBM_PEAK_GBS, 4), "traffic": paged_traffic},
         "roofline_backward": {"bound": "mfma", "achieved": round(btflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(btflops / MFMA_BF16_PEAK_TFLOPS, 4),
                               "traffic": bwd_traffic},
-        "mfma_util": {"prefill": mfma_use("prefill", pre_avg), "decode": mfma_use("decode", dec_avg),
+        "mfma_util": {"prefill": mfma_use("prefill", pre_avg), "varlen_prefill": mfma_use("varlen_prefill", var_ms),
+                      "decode": mfma_use("decode", dec_avg),
                       "decode_paged": mfma_use("decode_paged", paged_ms),
                       "backward": mfma_use("backward", bwd_ms)},
     }

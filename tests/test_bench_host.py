@@ -29,14 +29,24 @@ def test_paged_decode_bytes():
 def test_counter_dispatches_follow_the_launch_order():
     k = lambda s: "void fa::(anonymous namespace)::%s(int)" % s
     disp = {1: ("__amd_rocclr_copyBuffer", 1.0), 2: (k("prefill_bf16_kernel<128, true, false>"), 5.0),
-            3: (k("decode_split_kernel<128, false>"), 7.0), 4: (k("decode_combine_kernel<128>"), 1.0),
-            5: (k("paged_prep_kernel<128>"), 0.5), 6: (k("decode_split_kernel<128, true>"), 7.0),
-            7: (k("decode_combine_kernel<128>"), 1.0), 8: (k("bwd_pre_kernel<128>"), 2.0),
-            9: (k("bwd_dq_kernel<128, true, 4, 2>"), 3.0), 10: (k("bwd_dkdv_kernel<128, true, 8, 1>"), 4.0)}
+            3: (k("prefill_bf16_kernel<128, true, true>"), 6.0),
+            4: (k("decode_split_kernel<128, false>"), 7.0), 5: (k("decode_combine_kernel<128>"), 1.0),
+            6: (k("paged_prep_kernel<128>"), 0.5), 7: (k("decode_split_kernel<128, true>"), 7.0),
+            8: (k("decode_combine_kernel<128>"), 1.0), 9: (k("bwd_pre_kernel<128>"), 2.0),
+            10: (k("bwd_dq_kernel<128, true, 4, 2>"), 3.0), 11: (k("bwd_dkdv_kernel<128, true, 8, 1>"), 4.0)}
     parts = bench._part_of_dispatches(disp)
     assert 1 not in parts
-    assert [parts[i] for i in range(2, 11)] == ["prefill", "decode", "decode", "decode_paged", "decode_paged",
-                                                "decode_paged", "backward", "backward", "backward"]
+    assert [parts[i] for i in range(2, 12)] == ["prefill", "varlen_prefill", "decode", "decode", "decode_paged",
+                                                "decode_paged", "decode_paged", "backward", "backward", "backward"]
+
+
+def test_varlen_prefill_bytes():
+    cfg = inputs.VarlenConfig("t", torch.bfloat16, 2, 4, 2, 8, True, 3, 0, 0)
+    q_lens, k_lens = torch.tensor([3, 2]), torch.tensor([5, 1])
+    # Q and O: 5 rows x 4 heads x 8 x 2 B each; K and V: 6 rows x 2 heads x 8 x 2 B each;
+    # LSE: 5 x 4 floats; two offset arrays of 3 int32
+    expect = 2 * 5 * 4 * 8 * 2 + 2 * 6 * 2 * 8 * 2 + 5 * 4 * 4 + 2 * 3 * 4
+    assert bench.varlen_prefill_bytes(cfg, q_lens, k_lens) == expect
 
 
 def test_mfma_summary_sums_each_part(tmp_path, monkeypatch):

@@ -179,6 +179,29 @@ def test_peaked_softmax_rows(dtype):
         assert_close(lse, rl, tol_l, "LSE")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_jump_past_the_reference(d):
+    """Key magnitudes ramp up along the sequence (x1 at key 0 to x40 at the
+    last key, Q x3), so scores of later tiles exceed the reference that tile 0
+    set by far more than the lazy-rescale slack, again and again: the
+    reference moves and O, l are rescaled many times per row, on unmasked and
+    (causal) diagonal tiles alike.  Rows end dominated by single keys: O takes
+    the bf16 bound plus 2^-8 of |O| (its own rounding), LSE (up to several
+    hundred) the 1e-3 bound."""
+    B, Hq, Hkv, N = 1, 4, 2, 700
+    q, k, v = inputs.prefill_inputs(B, N, N, Hq, Hkv, d, torch.bfloat16, seed=11, q_mult=3.0)
+    ramp = torch.linspace(1.0, 40.0, N, dtype=torch.float64).view(1, N, 1, 1)
+    k = (k.double() * ramp).to(torch.bfloat16)
+    scale = inputs.fp32_scale(d)
+    _say("case: scores jump past the reference d=%d" % d)
+    for causal in (False, True):
+        o, lse = gpu_fwd(q, k, v, causal, scale)
+        ro, rl = oracle.attention(q, k, v, causal, scale)
+        assert float(rl.max()) > 200.0        # the scores did climb far past tile 0's
+        assert_close(o, ro, TOL[torch.bfloat16][0], "O", rel=2.0 ** -8)
+        assert_close(lse, rl, TOL[torch.bfloat16][1], "LSE")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_no_keys_gives_zero_and_minus_inf(dtype):
     q, k, v = inputs.prefill_inputs(2, 5, 0, 2, 1, 64, dtype)

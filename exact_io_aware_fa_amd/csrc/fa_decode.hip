@@ -55,6 +55,15 @@
 namespace fa {
 namespace {
 
+// Cache rows are read once per call and the cache is far larger than the
+// caches, so they are loaded non-temporal (policy bit NT): streamed rather
+// than allocated.  Measured after a prefill launch, this took the decode
+// workload from 0.360 to 0.321 ms: the streamed rows no longer push the
+// prefill's freshly written output out of the cache (as write-backs to HBM)
+// while the decode runs.
+__device__ __forceinline__ u32x4 load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
 constexpr int kTile = kDecodeTile;  // keys per tile
 constexpr int kGMax = 16;           // query heads per kv head (one MFMA column block)
 constexpr float kRescaleSlack = 8.0f;
@@ -185,9 +194,9 @@ __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
         t.nv = n - tile * kTile;
         const uint32_t base = (uint32_t)tile * kTile * rstride + ld_lane;
 #pragma unroll
-        for (int i = 0; i < VL; ++i) t.k[i] = buffer_load16(k_rsrc, base + i * RPL * rstride);
+        for (int i = 0; i < VL; ++i) t.k[i] = load16_stream(k_rsrc, base + i * RPL * rstride);
 #pragma unroll
-        for (int i = 0; i < VL; ++i) t.v[i] = buffer_load16(v_rsrc, base + i * RPL * rstride);
+        for (int i = 0; i < VL; ++i) t.v[i] = load16_stream(v_rsrc, base + i * RPL * rstride);
       } else {
         // the tile's rows: one block, found by one (scalar) table lookup; a
         // tile past the piece, past the table's row or with an entry outside
@@ -205,9 +214,9 @@ __global__ __launch_bounds__(64 * kMaxHW, 1) void decode_split_kernel(
         const __amdgpu_buffer_rsrc_t kr = make_rsrc(kc + (prow * Hkv + g) * D, tbytes);
         const __amdgpu_buffer_rsrc_t vr = make_rsrc(vc + (prow * Hkv + g) * D, tbytes);
 #pragma unroll
-        for (int i = 0; i < VL; ++i) t.k[i] = buffer_load16(kr, ld_lane + i * RPL * rstride);
+        for (int i = 0; i < VL; ++i) t.k[i] = load16_stream(kr, ld_lane + i * RPL * rstride);
 #pragma unroll
-        for (int i = 0; i < VL; ++i) t.v[i] = buffer_load16(vr, ld_lane + i * RPL * rstride);
+        for (int i = 0; i < VL; ++i) t.v[i] = load16_stream(vr, ld_lane + i * RPL * rstride);
       }
       // issue these loads before any of the following compute (the scheduler
       // would otherwise hoist the previous tile's first wait above them)

@@ -189,14 +189,18 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
 
   // ---- Q -> registers (B operands of S^T = K Q^T): lane (row j, group c)
   // holds head-dim 32t + 8c..+7 of row 16rb + j; absent rows (below 0) get an
-  // offset past any slice (slices are under 2 GiB) and read 0
+  // offset past any slice (slices are under 2 GiB) and read 0.  Q is read
+  // once, so its loads are non-temporal (policy bit NT): it is streamed
+  // rather than allocated in the caches that hold the re-read K/V tiles.
+  constexpr int kNT = 2;
   bf16x8 qf[kRB][DT];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     const int row = wbase + 16 * rb + l16;
     const uint32_t off = row >= 0 ? (uint32_t)row * q_row_bytes + grp * 16 : 0x80000000u;
 #pragma unroll
-    for (int t = 0; t < DT; ++t) qf[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(q_rsrc, off + t * 64));
+    for (int t = 0; t < DT; ++t)
+      qf[rb][t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off + t * 64, 0, kNT));
   }
 
   // ---- KV tiles this workgroup needs, and where this wave's masked suffix starts

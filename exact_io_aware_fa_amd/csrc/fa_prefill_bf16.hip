@@ -450,6 +450,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
     const int last_key0 = q0 + kRows * (kWaves / 2) - 1 + offs;   // group 0's last row's last key
     n0 = max(1, min(n_kv, last_key0 < 0 ? 0 : last_key0 / kBC + 1));
   }
+  // In a partial tile whose first half is all absent rows (below 0, never
+  // stored), group 0 has nothing to compute whatever those rows would see:
+  // it stops after one tile, causal or not.
+  if (PREFILL_EARLY_STOP && q0 + kRows * (kWaves / 2) <= 0) n0 = min(n0, 1);
   // Rounds of kNS tiles, unrolled so that every stage is named statically.
   // The check after each tile leaves the loop (it never skips ahead to the
   // next round), so at the top of a round, as far as the compiler can tell,

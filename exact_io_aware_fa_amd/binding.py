@@ -104,6 +104,33 @@ def _dev_ptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr()
 
 
+def _check_out(t: torch.Tensor, name: str, shape, dtype, like: torch.Tensor):
+    """A caller-given output must be exactly what the kernels write: the C ABI
+    receives only its pointer, so a smaller or differently typed buffer would
+    be written past its end."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device != like.device:
+        raise ValueError("%s must be on %s, got %s" % (name, like.device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_same_dtype(ref: torch.Tensor, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.dtype != ref.dtype:
+            raise TypeError("%s must share q's dtype %s, got %s" % (name, ref.dtype, t.dtype))
+
+
+def _check_workspace(ws: torch.Tensor, like: torch.Tensor):
+    if ws.device != like.device:
+        raise ValueError("workspace must be on %s, got %s" % (like.device, ws.device))
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+
+
 def _stream_handle(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -121,12 +148,13 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, scale: 
     if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
                                                              tuple(v.shape)))
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share a dtype")
+    _check_same_dtype(q, k=k, v=v)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, "out", q.shape, q.dtype, q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_out(lse, "lse", (B, Hq, N), torch.float32, q)
     st = lib.fa_fwd(_dtype_code(q), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(out),
                     _dev_ptr(lse), B, Hq, Hkv, N, Nk, d, 1 if causal else 0, float(scale),
                     _stream_handle(stream))
@@ -148,8 +176,7 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
     if dk != d or tuple(v.shape) != tuple(k.shape):
         raise ValueError("shape mismatch: q %s k %s v %s" % (tuple(q.shape), tuple(k.shape),
                                                              tuple(v.shape)))
-    if not (q.dtype == k.dtype == v.dtype):
-        raise TypeError("q, k, v must share a dtype")
+    _check_same_dtype(q, k=k, v=v)
     for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
         if cu.dtype != torch.int32 or cu.dim() != 1:
             raise ValueError("%s must be a 1-D int32 tensor" % name)
@@ -158,8 +185,10 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: 
     B = cu_seqlens_q.numel() - 1
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, "out", q.shape, q.dtype, q)
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    _check_out(lse, "lse", (Hq, total_q), torch.float32, q)
     st = lib.fa_fwd_varlen(_dtype_code(q), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(cu_seqlens_q),
                            _dev_ptr(cu_seqlens_k), int(max_seqlen_q), int(max_seqlen_k), total_q, total_k,
                            _dev_ptr(out), _dev_ptr(lse), B, Hq, Hkv, d, 1 if causal else 0, float(scale),
@@ -189,15 +218,19 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         raise ValueError("shape mismatch between q and caches")
     if cu_seqlens_k.dtype != torch.int32 or cu_seqlens_k.numel() != B + 1:
         raise ValueError("cu_seqlens_k must be int32 with B+1 entries")
+    _check_same_dtype(q, k_cache=k_cache, v_cache=v_cache)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, "out", q.shape, q.dtype, q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out(lse, "lse", (B, Hq), torch.float32, q)
     # no sequence can be longer than the cache holds rows
     max_seqlen_k = min(int(max_seqlen_k), total)
     need = int(lib.fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q)
     st = lib.fa_decode(_dtype_code(q), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),
                        _dev_ptr(cu_seqlens_k), int(max_seqlen_k), _dev_ptr(out), _dev_ptr(lse),
                        B, Hq, Hkv, d, float(scale), _dev_ptr(workspace),
@@ -234,13 +267,17 @@ def decode_paged(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
         raise ValueError("block_table must be int32 [B, max_blocks]")
     if seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B:
         raise ValueError("seqlens_k must be int32 with B entries")
+    _check_same_dtype(q, k_cache=k_cache, v_cache=v_cache, k_new=k_new, v_new=v_new)
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, "out", q.shape, q.dtype, q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out(lse, "lse", (B, Hq), torch.float32, q)
     need = int(lib.fa_decode_paged_workspace_bytes(B, Hq, Hkv, d, int(max_seqlen_k)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q)
     st = lib.fa_decode_paged(_dtype_code(q), _dev_ptr(q), _dev_ptr(k_new), _dev_ptr(v_new), _dev_ptr(k_cache),
                              _dev_ptr(v_cache), _dev_ptr(block_table), _dev_ptr(seqlens_k), num_blocks, block_size,
                              block_table.shape[1], int(max_seqlen_k), _dev_ptr(out), _dev_ptr(lse), B, Hq, Hkv, d,
@@ -267,12 +304,17 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
         raise ValueError("o and dout must have q's shape")
     if tuple(lse.shape) != (B, Hq, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be fp32 [B, Hq, N]")
+    _check_same_dtype(q, k=k, v=v, o=o, dout=dout)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_out(dq, "dq", q.shape, q.dtype, q)
+    _check_out(dk, "dk", k.shape, q.dtype, q)
+    _check_out(dv, "dv", v.shape, q.dtype, q)
     need = int(lib.fa_bwd_workspace_bytes(B, Hq, N))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, q)
     st = lib.fa_bwd(_dtype_code(q), _dev_ptr(q), _dev_ptr(k), _dev_ptr(v), _dev_ptr(o), _dev_ptr(lse),
                     _dev_ptr(dout), _dev_ptr(dq), _dev_ptr(dk), _dev_ptr(dv), B, Hq, Hkv, N, Nk, d,
                     1 if causal else 0, float(scale), _dev_ptr(workspace),

@@ -386,7 +386,8 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
   // is invisible to its first row: i0 + offs < kw + KEYS_W - 1
 
   const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
-  const uint32_t q_bytes = (uint32_t)((N - 1) * Hq + 1) * D * 2;
+  // (N = 0: no query tile is loaded, n_it = 0; the view is then empty)
+  const uint32_t q_bytes = N > 0 ? (uint32_t)((N - 1) * Hq + 1) * D * 2 : 0u;
   auto head_rsrc = [&](const uint16_t* base, int h) {
     return make_rsrc(base + ((int64_t)b * N * Hq + h) * D, q_bytes);
   };
@@ -607,12 +608,15 @@ hipError_t launch(const BwdArgs& a) {
     const int n_qtiles = (a.N + ROWS_G - 1) / ROWS_G;
     const int64_t n_work = (int64_t)a.B * a.Hq * n_qtiles;
     const int64_t grid = (n_work + 7) / 8 * 8;
-    if (grid == 0) return hipSuccess;                // no query rows: no dQ, and dK = dV = 0 below
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, kWQ, kRBQ>), dim3((unsigned)grid), dim3(64 * kWQ), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                       a.lse2, a.dsum, (uint16_t*)a.dq, a.N, a.Nk, a.Hq, a.Hkv, c, a.scale, n_qtiles, (int)n_work);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // (no query rows: no dQ to compute; the dK/dV kernel below still runs and
+    // writes dK = dV = 0, since no query sees any key)
+    if (grid > 0) {
+      hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, kWQ, kRBQ>), dim3((unsigned)grid), dim3(64 * kWQ), 0, a.stream,
+                         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                         a.lse2, a.dsum, (uint16_t*)a.dq, a.N, a.Nk, a.Hq, a.Hkv, c, a.scale, n_qtiles, (int)n_work);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (a.Nk > 0) {
     constexpr int KEYS_G = 16 * kRBK * kWK;

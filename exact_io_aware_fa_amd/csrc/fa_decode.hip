@@ -398,11 +398,16 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(
   M = fmaxf(M, __shfl_xor(M, 1, 64));
   // each lane weighs its piece; then every lane folds the chunk's pieces for
   // its head-dim values, reading each piece's weight and slot from its lane
+  // An absent piece (a lane past the last piece, or an empty range) takes the
+  // slot of piece 0 with weight 0: that slot is always written by this call,
+  // so the product with the zero weight reads a finite value (a slot no piece
+  // wrote may hold anything, Inf or NaN included, and 0 * Inf is NaN).
   float acc[PER] = {}, wlane_sum = 0.0f;
+  const int slot0 = (int)slot_of(0);
   for (int c0 = 0; c0 < npieces; c0 += 64) {
     const int i = c0 + lane;
     const bool ok = i < npieces && present(i);
-    const int sl = ok ? (int)slot_of(i) : 0;
+    const int sl = ok ? (int)slot_of(i) : slot0;
     const float ls = ok ? part_lse[sl] : -INFINITY;
     const float w = ls == -INFINITY ? 0.0f : fast_exp2((ls - M) * kLog2e);
     wlane_sum += w;

@@ -183,6 +183,91 @@ def test_binding_refuses_cpu_tensors(fa_lib):
         binding.fwd(q, q[:, :, :1].contiguous(), q[:, :, :1].contiguous(), False, 0.125)
 
 
+
+# Caller-given outputs and mixed input dtypes are refused by the binding before
+# any pointer reaches the library (an undersized or differently typed output
+# would otherwise be written past its end).  CPU tensors suffice: these checks
+# run before the device check.
+def _bf(*shape):
+    import torch
+    return torch.zeros(*shape, dtype=torch.bfloat16)
+
+
+def test_binding_checks_fwd_outputs_and_dtypes(fa_lib):
+    import torch
+    q, k = _bf(1, 4, 2, 64), _bf(1, 4, 1, 64)
+    with pytest.raises(ValueError, match="out must have shape"):
+        binding.fwd(q, k, k, False, 0.125, out=_bf(1, 3, 2, 64))
+    with pytest.raises(TypeError, match="out must be"):
+        binding.fwd(q, k, k, False, 0.125, out=torch.zeros(1, 4, 2, 64))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        binding.fwd(q, k, k, False, 0.125, lse=torch.zeros(1, 2, 3))
+    with pytest.raises(TypeError, match="lse must be"):
+        binding.fwd(q, k, k, False, 0.125, lse=torch.zeros(1, 2, 4, dtype=torch.float64))
+    with pytest.raises(ValueError, match="contiguous"):
+        binding.fwd(q, k, k, False, 0.125, out=_bf(1, 4, 64, 2).transpose(2, 3))
+    with pytest.raises(TypeError, match="k must share"):
+        binding.fwd(q, k.float(), k, False, 0.125)
+
+
+def test_binding_checks_varlen_outputs(fa_lib):
+    import torch
+    q, k = _bf(6, 2, 64), _bf(9, 1, 64)
+    cu = torch.tensor([0, 6], dtype=torch.int32)
+    cuk = torch.tensor([0, 9], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        binding.fwd_varlen(q, k, k, cu, cuk, 6, 9, True, 0.125, out=_bf(5, 2, 64))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        binding.fwd_varlen(q, k, k, cu, cuk, 6, 9, True, 0.125, lse=torch.zeros(6, 2))
+    with pytest.raises(TypeError, match="v must share"):
+        binding.fwd_varlen(q, k, k.float(), cu, cuk, 6, 9, True, 0.125)
+
+
+def test_binding_checks_decode_outputs_and_dtypes(fa_lib):
+    import torch
+    q, kc = _bf(2, 8, 128), _bf(40, 2, 128)
+    cu = torch.tensor([0, 10, 40], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        binding.decode(q, kc, kc, cu, 30, 0.1, out=_bf(1, 8, 128))
+    with pytest.raises(TypeError, match="out must be"):
+        binding.decode(q, kc, kc, cu, 30, 0.1, out=torch.zeros(2, 8, 128))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        binding.decode(q, kc, kc, cu, 30, 0.1, lse=torch.zeros(2, 4))
+    with pytest.raises(TypeError, match="k_cache must share"):
+        binding.decode(q, kc.float(), kc, cu, 30, 0.1)
+
+
+def test_binding_checks_decode_paged_outputs_and_dtypes(fa_lib):
+    import torch
+    q, pages, new = _bf(2, 8, 128), _bf(4, 64, 2, 128), _bf(2, 2, 128)
+    table = torch.zeros(2, 2, dtype=torch.int32)
+    lens = torch.tensor([10, 20], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        binding.decode_paged(q, pages, pages, table, lens, 20, 0.1, new, new, out=_bf(2, 8, 64))
+    with pytest.raises(ValueError, match="lse must have shape"):
+        binding.decode_paged(q, pages, pages, table, lens, 20, 0.1, new, new, lse=torch.zeros(8))
+    with pytest.raises(TypeError, match="k_new must share"):
+        binding.decode_paged(q, pages, pages, table, lens, 20, 0.1, new.float(), new)
+    with pytest.raises(TypeError, match="v_cache must share"):
+        binding.decode_paged(q, pages, pages.float(), table, lens, 20, 0.1, new, new)
+
+
+def test_binding_checks_bwd_outputs_and_dtypes(fa_lib):
+    import torch
+    q, k = _bf(1, 4, 2, 64), _bf(1, 5, 1, 64)
+    lse = torch.zeros(1, 2, 4)
+    with pytest.raises(TypeError, match="dout must share"):
+        binding.bwd(q, k, k, q, lse, q.float(), True, 0.125)
+    with pytest.raises(TypeError, match="o must share"):
+        binding.bwd(q, k, k, q.float(), lse, q, True, 0.125)
+    with pytest.raises(ValueError, match="dq must have shape"):
+        binding.bwd(q, k, k, q, lse, q, True, 0.125, dq=_bf(1, 4, 2, 32))
+    with pytest.raises(ValueError, match="dk must have shape"):
+        binding.bwd(q, k, k, q, lse, q, True, 0.125, dk=_bf(1, 4, 1, 64))
+    with pytest.raises(TypeError, match="dv must be"):
+        binding.bwd(q, k, k, q, lse, q, True, 0.125, dv=torch.zeros(1, 5, 1, 64))
+
+
 def _paged(lib, dtype=BF16, q=None, kn=None, vn=None, kc=None, vc=None, table=None, lens=None, num_blocks=8,
            block_size=64, max_blocks=4, max_len=200, o=None, lse=None, B=2, Hq=8, Hkv=2, d=128, scale=0.1, ws=None,
            ws_bytes=0):

@@ -134,3 +134,20 @@ def test_bwd_llama70b_shape_one_kv_head_full_size():
     assert_grad_close(dv[:, :, :1], rv, mv, "dV (kv head 0)")
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_bwd_no_queries_gives_zero_key_gradients(causal):
+    """N = 0 with keys present: no query sees any key, so dk = dv = 0; the
+    outputs start as NaN so that an unwritten element shows."""
+    d = 128
+    q = torch.zeros((1, 0, 4, d), dtype=torch.bfloat16, device="cuda")
+    k = _dout((1, 64, 2, d), 40).cuda()
+    v = _dout((1, 64, 2, d), 41).cuda()
+    o = torch.zeros_like(q)
+    lse = torch.zeros((1, 4, 0), dtype=torch.float32, device="cuda")
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    binding.bwd(q, k, v, o, lse, o, causal, inputs.fp32_scale(d), dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)

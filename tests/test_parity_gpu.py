@@ -379,6 +379,32 @@ def test_decode_matches_single_query_prefill():
         assert (lse[b] - lp[0, :, 0]).abs().max() <= 1e-3
 
 
+
+@pytest.mark.parametrize("fill", [float("nan"), float("inf")], ids=["nan", "inf"])
+def test_decode_fewer_keys_than_ranges_with_dirty_workspace(fill):
+    """When the cache holds fewer keys than the plan has key ranges (short
+    caches with a large max_seqlen_k bound), some ranges are empty; the merge
+    must not read a partial slot that no range wrote.  The workspace starts
+    filled with NaN or Inf, as reused memory may be."""
+    lens = [1000] + [1] * 63
+    Hq, Hkv, d = 8, 1, 128
+    _say("case: decode, fewer keys than ranges, workspace filled with %s" % fill)
+    q, kc, vc, cu = inputs.decode_inputs(lens, Hq, Hkv, d, torch.bfloat16, seed=31)
+    total, rows = int(cu[-1]), 8192
+    kbig = torch.zeros((rows, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    vbig = torch.zeros((rows, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    kbig[:total] = kc.cuda()
+    vbig[:total] = vc.cuda()
+    max_len = rows                                        # a valid upper bound of every length
+    ws_bytes = binding.decode_workspace_bytes(len(lens), Hq, Hkv, d, max_len)
+    ws = torch.full(((ws_bytes + 3) // 4,), fill, dtype=torch.float32, device="cuda").view(torch.uint8)
+    o, lse = binding.decode(q.cuda(), kbig, vbig, cu.cuda(), max_len, inputs.fp32_scale(d), workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(q, kc, vc, cu, inputs.fp32_scale(d))
+    assert_close(o.cpu(), ro, 1e-2, "O")
+    assert_close(lse.cpu(), rl, 1e-3, "LSE")
+
+
 # --------------------------------------------- paged cache, new row appended
 
 def gpu_decode_paged(x, scale, append=True, table=None):
@@ -478,6 +504,30 @@ def test_paged_decode_entry_outside_the_cache_is_an_absent_block():
     assert_close(lse, rl, 1e-3, "LSE")
     ek, ev = expected_pages(x, True)
     assert torch.equal(_bits(kp), _bits(ek)) and torch.equal(_bits(vp), _bits(ev))
+
+
+@pytest.mark.parametrize("fill", [float("nan"), float("inf")], ids=["nan", "inf"])
+def test_paged_decode_fewer_tiles_than_ranges_with_dirty_workspace(fill):
+    """One long and many one-row caches on one kv head: the plan has more key
+    ranges (2048) than the cache has 32-key tiles, so some ranges are empty and
+    the merge must skip them without reading an unwritten partial slot.  The
+    workspace starts filled with NaN or Inf."""
+    lens = [32768 - 1] + [32] * 63
+    Hq, Hkv, d, bs = 8, 1, 128, 64
+    _say("case: paged decode, fewer tiles than ranges, workspace filled with %s" % fill)
+    x = inputs.paged_decode_inputs(lens, Hq, Hkv, d, bs, torch.bfloat16, seed=32)
+    scale = inputs.fp32_scale(d)
+    max_len = max(lens)
+    B = len(lens)
+    ws_bytes = binding.decode_paged_workspace_bytes(B, Hq, Hkv, d, max_len)
+    ws = torch.full(((ws_bytes + 3) // 4,), fill, dtype=torch.float32, device="cuda").view(torch.uint8)
+    kp, vp = x["k_pages"].cuda(), x["v_pages"].cuda()
+    o, lse = binding.decode_paged(x["q"].cuda(), kp, vp, x["block_table"].cuda(), x["seqlens"].cuda(), max_len,
+                                  scale, x["k_new"].cuda(), x["v_new"].cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    ro, rl, _, _, _ = oracle.decode_append(x["q"], x["kc"], x["vc"], x["cu"], x["k_new"], x["v_new"], scale)
+    assert_close(o.cpu(), ro, 1e-2, "O")
+    assert_close(lse.cpu(), rl, 1e-3, "LSE")
 
 
 def test_paged_decode_workload_full_size_sampled():

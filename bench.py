@@ -269,6 +269,96 @@ def paged_decode_bytes(cfg, lens, block_size):
             + cfg.B * 4 + blocks * 4)
 
 
+
+FP32_VALU_PEAK_TFLOPS = 157.3      # MI355X fp32 vector peak (256 CUs x 256 flop/clk x 2.4 GHz)
+# The three small prefill workloads, each timed on rotated input copies whose
+# total size exceeds the 256 MB Infinity Cache, so that every launch reads its
+# inputs from HBM (the configs' algorithmic bytes are 0.26 MB, 68 MB, 51 MB).
+SMALL_PREFILL = (("single_head_fp32", "SINGLE_HEAD_F32", 1),
+                 ("bert_large_bf16", "BERT_LARGE_BF16", 5),
+                 ("gpt2_causal_bf16", "GPT2_CAUSAL_BF16", 6))
+
+
+def prefill_bytes(cfg, elem_bytes):
+    """Algorithmic bytes of one prefill launch: Q, K, V read once, O and LSE
+    (fp32) written once."""
+    qo = 2 * cfg.B * cfg.N * cfg.Hq * cfg.d * elem_bytes
+    kv = 2 * cfg.B * cfg.Nk * cfg.Hkv * cfg.d * elem_bytes
+    return qo + kv + cfg.B * cfg.Hq * cfg.N * 4
+
+
+def device_info(torch):
+    """The GPU's own figures, and the peaks derived from them: bf16 dense MFMA
+    = CUs x peak clock x 4096 flop/clk/CU; HBM = memory clock x 2 (double data
+    rate) x bus width / 8."""
+    pr = torch.cuda.get_device_properties(0)
+    cus, clk_khz = int(pr.multi_processor_count), int(getattr(pr, "clock_rate", 0))
+    mem_khz, bus = int(getattr(pr, "memory_clock_rate", 0)), int(getattr(pr, "memory_bus_width", 0))
+    if not (clk_khz and mem_khz and bus):
+        # torch leaves these at 0 on ROCm: ask HIP (hipDeviceGetAttribute with the
+        # HIP 7 enum values of ClockRate, MemoryClockRate, MemoryBusWidth)
+        import ctypes
+        try:
+            hip = ctypes.CDLL("libamdhip64.so")
+            val = ctypes.c_int()
+            got = {}
+            for name, attr in (("clk", 5), ("mem", 60), ("bus", 59)):
+                got[name] = val.value if hip.hipDeviceGetAttribute(ctypes.byref(val), attr, 0) == 0 else 0
+            clk_khz, mem_khz, bus = got["clk"] or clk_khz, got["mem"] or mem_khz, got["bus"] or bus
+        except OSError:
+            pass
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "cus": cus, "clock_mhz": clk_khz / 1000.0,
+            "memory_clock_mhz": mem_khz / 1000.0, "memory_bus_width_bits": bus,
+            "peak_bf16_tflops_derived": round(cus * clk_khz * 1e3 * 4096 / 1e12, 1),
+            "peak_hbm_gbs_derived": round(mem_khz * 1e3 * 2 * bus / 8 / 1e9, 1),
+            "peak_bf16_tflops_spec": MFMA_BF16_PEAK_TFLOPS, "peak_hbm_gbs_spec": HBM_PEAK_GBS}
+
+
+def time_small_prefill(torch, binding, inputs, dev, cfg, copies, steps, warmup):
+    """Mean launch time (ms) of fa_fwd on `cfg`, each launch on the next of
+    `copies` device copies of the same seeded inputs."""
+    q, k, v = inputs.prefill_config_inputs(cfg)
+    sets = []
+    for _ in range(copies):
+        qd = q.to(dev)
+        sets.append((qd, k.to(dev), v.to(dev), torch.empty_like(qd),
+                     torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)))
+    for i in range(max(warmup, copies)):
+        a = sets[i % copies]
+        binding.fwd(a[0], a[1], a[2], cfg.causal, cfg.scale, out=a[3], lse=a[4])
+    torch.cuda.synchronize()
+    n = max(steps, 4 * copies)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        a = sets[i % copies]
+        binding.fwd(a[0], a[1], a[2], cfg.causal, cfg.scale, out=a[3], lse=a[4])
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def small_prefill_entry(cfg, ms, copies):
+    """roofline object of a small prefill workload: fp32 against the vector
+    ALU peak; bf16 against HBM (its intensity, 254 flop/B, is below the bf16
+    ridge of about 312 flop/B) with the MFMA fraction beside it."""
+    flops = prefill_flops(cfg)
+    tflops = flops / (ms * 1e-3) / 1e12
+    if cfg.dtype.itemsize == 4:
+        nbytes = prefill_bytes(cfg, 4)
+        return {"bound": "alu", "achieved": round(tflops, 4), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 5), "traffic": None, "ms": round(ms, 5),
+                "flops_per_launch": flops, "bytes_per_launch": nbytes,
+                "note": "one launch of one 256-row head: bound by launch and per-key latency, not by the ALU"}
+    nbytes = prefill_bytes(cfg, 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "ms": round(ms, 5),
+            "hbm_floor_us": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+            "tflops": round(tflops, 1), "frac_mfma": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_launch": flops, "bytes_per_launch": nbytes, "input_copies": copies}
+
+
 def varlen_flops(cfg, q_lens, k_lens):
     """4*d*Hq per visible (query, key) pair; causal is bottom-right per sequence."""
     pairs = 0
@@ -293,9 +383,17 @@ def cpu_baseline(q, k, v, cfg):
     t0 = time.perf_counter()
     oracle.attention_rows(q, k, v, cfg.causal, cfg.scale, rows, nthreads=threads)
     dt = time.perf_counter() - t0
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)), "os_cpu_count": os.cpu_count(),
             "sample": "%d query rows (every 8th row x %d heads) of the prefill workload, "
-                      "%.1f s wall" % (len(rows), cfg.Hq, dt)}
+                      "%.1f s wall; threads = the CPUs this process may use, capped at 16 "
+                      "(the host share of one GPU)" % (len(rows), cfg.Hq, dt)}
 
 
 def setup_varlen(torch, binding, inputs, dev):
@@ -497,6 +595,18 @@ def main():
     bflops = 2.5 * flops
     btflops = bflops / (bwd_ms * 1e-3) / 1e12
 
+    # the three small prefill workloads, each on rotated input copies
+    del backward
+    small = {}
+    for key, attr, copies in SMALL_PREFILL:
+        scfg = getattr(inputs, attr)
+        small[key] = small_prefill_entry(scfg, time_small_prefill(torch, binding, inputs, dev, scfg, copies, K,
+                                                                  args.warmup), copies)
+        small[key]["config"] = {"B": scfg.B, "Hq": scfg.Hq, "Hkv": scfg.Hkv, "N": scfg.N, "Nk": scfg.Nk,
+                                "d": scfg.d, "causal": scfg.causal,
+                                "dtype": str(scfg.dtype).replace("torch.", "")}
+        torch.cuda.empty_cache()
+
     pre_traffic = measured_traffic("prefill")
     var_traffic = measured_traffic("varlen_prefill")
     dec_traffic = measured_traffic("decode")
@@ -557,6 +667,10 @@ def main():
         "roofline_backward": {"bound": "mfma", "achieved": round(btflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(btflops / MFMA_BF16_PEAK_TFLOPS, 4),
                               "traffic": bwd_traffic},
+        "roofline_c1_single_head_fp32": small["single_head_fp32"],
+        "roofline_c2_bert_large_bf16": small["bert_large_bf16"],
+        "roofline_c3_gpt2_causal_bf16": small["gpt2_causal_bf16"],
+        "device": device_info(torch),
         "mfma_util": {"prefill": mfma_use("prefill", pre_avg), "varlen_prefill": mfma_use("varlen_prefill", var_ms),
                       "decode": mfma_use("decode", dec_avg),
                       "decode_paged": mfma_use("decode_paged", paged_ms),

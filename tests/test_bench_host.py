@@ -77,3 +77,26 @@ def test_mfma_summary_sums_each_part(tmp_path, monkeypatch):
     assert out["decode"]["bf16_mfma_flops"] == 0.0
     monkeypatch.setattr(bench, "MFMA_FILE", str(tmp_path / "mfma.json"))
     assert bench.measured_mfma_flops("backward") == 2.4e6 * 512
+
+
+def test_small_prefill_bytes_and_floors():
+    """Algorithmic bytes of the three small workloads: Q, K, V read once, O and
+    LSE written once, and the HBM floor of the bf16 ones at 8 TB/s."""
+    c1, c2, c3 = inputs.SINGLE_HEAD_F32, inputs.BERT_LARGE_BF16, inputs.GPT2_CAUSAL_BF16
+    assert bench.prefill_bytes(c1, 4) == 4 * 256 * 64 * 4 + 256 * 4 == 263168
+    assert bench.prefill_bytes(c2, 2) == 4 * 16 * 512 * 16 * 64 * 2 + 16 * 16 * 512 * 4 == 67633152
+    assert bench.prefill_bytes(c3, 2) == 4 * 8 * 1024 * 12 * 64 * 2 + 8 * 12 * 1024 * 4 == 50724864
+    e2 = bench.small_prefill_entry(c2, 0.0169, 5)
+    assert e2["bound"] == "hbm" and e2["hbm_floor_us"] == 8.45
+    assert abs(e2["frac"] - 67633152 / 0.0169e-3 / 8e12) < 1e-4
+    assert abs(e2["frac_mfma"] - 2 ** 34 / 0.0169e-3 / 2.5e15) < 1e-4
+    e1 = bench.small_prefill_entry(c1, 0.04, 1)
+    assert e1["bound"] == "alu" and e1["peak"] == 157.3
+
+
+def test_small_prefill_copies_exceed_the_infinity_cache():
+    """The rotated input copies of each bf16 workload together exceed 256 MB."""
+    for key, attr, copies in bench.SMALL_PREFILL:
+        cfg = getattr(inputs, attr)
+        if cfg.dtype == torch.bfloat16:
+            assert copies * bench.prefill_bytes(cfg, 2) > 256 * 2 ** 20, key

@@ -12,6 +12,7 @@ import torch.nn.functional as F
 
 from exact_io_aware_fa_amd import inputs
 from oracle import oracle
+from tests import brute
 
 
 def _rand(shape, seed):
@@ -107,3 +108,71 @@ def test_bwd_magnitudes_bound_the_gradients_and_head_subset():
     sq, sk, sv = oracle.attention_bwd(q, k, v, do, True, 0.3, kv_heads=[1])
     assert np.array_equal(sq[:, :, 2:], dq[:, :, 2:]) and np.all(sq[:, :, :2] == 0)
     assert np.array_equal(sk[:, :, 1], dk[:, :, 1]) and np.array_equal(sv[:, :, 1], dv[:, :, 1])
+
+
+MAG_CASES = [
+    # (B, Hq, Hkv, N, Nk, causal)
+    (1, 2, 1, 3, 4, False),
+    (1, 2, 1, 4, 3, True),       # N > Nk: a leading row sees no key
+    (2, 4, 2, 3, 5, True),       # GQA groups of 2, bottom-right causal
+]
+
+
+def _magnitudes_vs_brute(fn, case, seed=7):
+    B, Hq, Hkv, N, Nk, causal = case
+    d, scale = 4, 0.6
+    q, k, v = inputs.prefill_inputs(B, N, Nk, Hq, Hkv, d, torch.float64, seed=seed)
+    do = _rand(q.shape, seed + 1)
+    _, _, _, (mq, mk, mv) = fn(q, k, v, do, causal, scale, with_magnitudes=True)
+    bq, bk, bv = brute.bwd_magnitudes(q.tolist(), k.tolist(), v.tolist(), do.tolist(), causal, scale)
+    worst = 0.0
+    for got, ref in ((mq, bq), (mk, bk), (mv, bv)):
+        ref = np.asarray(ref)
+        worst = max(worst, float(np.abs(got - ref).max() / max(1.0, np.abs(ref).max())))
+    return worst
+
+
+@pytest.mark.parametrize("case", MAG_CASES, ids=lambda c: "B%dHq%dHkv%dN%dNk%d%s" % (c[:5] + ("c" if c[5] else "",)))
+def test_bwd_magnitudes_match_the_scalar_brute_force(case):
+    """The magnitude sums that set every backward GPU tolerance equal, at
+    1e-12, the same sums taken term by term in plain Python loops: pinned from
+    above as well as from below."""
+    assert _magnitudes_vs_brute(oracle.attention_bwd, case) <= 1e-12
+
+
+# Planted mistakes in the magnitude sums (each would loosen every backward
+# tolerance without failing the gradient pins): the scalar brute force above
+# must reject each.
+BWD_MUTANTS = {
+    "scale dropped from mq": ("mq[b, :, h, :] = scale * ((aS + a * P) @ np.abs(Kg))",
+                              "mq[b, :, h, :] = ((aS + a * P) @ np.abs(Kg))"),
+    "scale dropped from mk": ("mk[b, :, g, :] += scale * ((aS + a * P).T @ np.abs(Qh))",
+                              "mk[b, :, g, :] += ((aS + a * P).T @ np.abs(Qh))"),
+    "D term doubled": ("a = np.abs(dOh * (P @ Vg)).sum(axis=1, keepdims=True)",
+                       "a = 2 * np.abs(dOh * (P @ Vg)).sum(axis=1, keepdims=True)"),
+    "D term dropped": ("mq[b, :, h, :] = scale * ((aS + a * P) @ np.abs(Kg))",
+                       "mq[b, :, h, :] = scale * (aS @ np.abs(Kg))"),
+    "dV magnitude without abs": ("mv[b, :, g, :] += P.T @ np.abs(dOh)", "mv[b, :, g, :] += P.T @ dOh"),
+}
+
+
+def _mutant_bwd(old, new):
+    """attention_bwd from a copy of oracle.py's source with one edit (the copy is
+    executed on the CPU in its own namespace; the oracle itself is unchanged)."""
+    import os
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.py")).read()
+    assert src.count(old) == 1, old
+    ns = {"__name__": "oracle_bwd_mutant", "__file__": oracle.__file__}
+    exec(compile(src.replace(old, new), "oracle_bwd_mutant", "exec"), ns)
+    return ns["attention_bwd"]
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_magnitude_mutants_are_caught(name):
+    fn = _mutant_bwd(*BWD_MUTANTS[name])
+    assert max(_magnitudes_vs_brute(fn, c) for c in MAG_CASES) > 1e-6, name
+
+
+def test_bwd_magnitude_mutant_harness_accepts_the_oracle():
+    fn = _mutant_bwd("mv[b, :, g, :] += P.T @ np.abs(dOh)", "mv[b, :, g, :] += P.T @ np.abs(dOh)")
+    assert max(_magnitudes_vs_brute(fn, c) for c in MAG_CASES) <= 1e-12

@@ -16,7 +16,7 @@ _LIBNAME = "libfa.so"
 
 FA_F32, FA_BF16 = 0, 1
 FA_OK = 0
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 
@@ -52,6 +52,8 @@ def load_library():
     lib.fa_fwd_varlen.restype = i32
     lib.fa_decode.argtypes = [i32, p, p, p, p, i32, p, p, i32, i32, i32, i32, f32, p, sz, p]
     lib.fa_decode.restype = i32
+    lib.fa_decode_noalloc.argtypes = [i32, p, p, p, p, i32, p, p, i32, i32, i32, i32, f32, p]
+    lib.fa_decode_noalloc.restype = i32
     lib.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode_paged.argtypes = [i32, p, p, p, p, p, p, p, i32, i32, i32, i32, p, p, i32, i32, i32, i32, f32,
@@ -239,6 +241,41 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _raise(lib, st)
     return out, lse
 
+
+
+DECODE_SCRATCH_BYTES = 16 << 20     # FA_DECODE_SCRATCH_BYTES in include/fa.h
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   cu_seqlens_k: torch.Tensor, max_seqlen_k: int, scale: float,
+                   out: torch.Tensor | None = None, lse: torch.Tensor | None = None, stream=None):
+    """``decode`` without a workspace argument: the partial results go to the
+    library's static device array (fa_decode_noalloc).  With ``out`` and ``lse``
+    given the call allocates nothing.  Calls that overlap on one GPU race on
+    that array; order them on one stream."""
+    lib = load_library()
+    if q.dim() != 3 or k_cache.dim() != 3 or v_cache.dim() != 3:
+        raise ValueError("q must be [B,Hq,d] and caches [total,Hkv,d]")
+    B, Hq, d = q.shape
+    total, Hkv, dk = k_cache.shape
+    if dk != d or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("shape mismatch between q and caches")
+    if cu_seqlens_k.dtype != torch.int32 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_k must be int32 with B+1 entries")
+    _check_same_dtype(q, k_cache=k_cache, v_cache=v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_out(out, "out", q.shape, q.dtype, q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_out(lse, "lse", (B, Hq), torch.float32, q)
+    max_seqlen_k = min(int(max_seqlen_k), total)
+    st = lib.fa_decode_noalloc(_dtype_code(q), _dev_ptr(q), _dev_ptr(k_cache), _dev_ptr(v_cache),
+                               _dev_ptr(cu_seqlens_k), int(max_seqlen_k), _dev_ptr(out), _dev_ptr(lse),
+                               B, Hq, Hkv, d, float(scale), _stream_handle(stream))
+    if st != FA_OK:
+        _raise(lib, st)
+    return out, lse
 
 def decode_paged_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_seqlen_k: int) -> int:
     return int(load_library().fa_decode_paged_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k))

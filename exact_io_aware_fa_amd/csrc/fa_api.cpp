@@ -185,10 +185,13 @@ FA_EXPORT size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int ma
   return decode_layout(B, Hq, Hkv, d, max_seqlen_k).bytes;
 }
 
-FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_cache, const void* v_cache,
-                                const int32_t* cu_seqlens_k, int max_seqlen_k, void* o, float* lse, int B,
-                                int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+namespace {
+
+// fa_decode and fa_decode_noalloc: the same checks and launch; the second takes
+// its workspace from the library's static device array (scratch != false).
+fa_status_t decode_impl(fa_dtype_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cu_seqlens_k, int max_seqlen_k, void* o, float* lse, int B, int Hq, int Hkv,
+                        int d, float scale, void* workspace, size_t workspace_bytes, void* stream, bool scratch) {
   if (dtype != FA_F32 && dtype != FA_BF16) return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (B < 0 || max_seqlen_k < 0) return fail(FA_ERR_INVALID_ARG, "negative size (B=%d max_seqlen_k=%d)", B, max_seqlen_k);
   if (Hq <= 0 || Hkv <= 0) return fail(FA_ERR_INVALID_ARG, "head counts must be positive (Hq=%d Hkv=%d)", Hq, Hkv);
@@ -210,14 +213,27 @@ FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_c
   if ((reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u) != 0)
     return fail(FA_ERR_INVALID_ARG, "cu_seqlens_k must be 4-byte aligned");
   const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_seqlen_k);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0, need);
   const size_t qo_bytes = (size_t)B * Hq * d * 2;
   const size_t lse_bytes = (size_t)B * Hq * sizeof(float);
+  if (scratch) {
+    workspace = nullptr;
+    if (need > FA_DECODE_SCRATCH_BYTES)
+      return fail(FA_ERR_WORKSPACE, "these sizes need %zu bytes of scratch; the static array holds %zu "
+                  "(use fa_decode with a caller-owned workspace)", need, (size_t)FA_DECODE_SCRATCH_BYTES);
+  } else if (need > 0 && (!workspace || workspace_bytes < need)) {
+    return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace ? workspace_bytes : (size_t)0,
+                need);
+  }
   if (overlaps(o, qo_bytes, q, qo_bytes) || overlaps(lse, lse_bytes, q, qo_bytes) ||
       overlaps(lse, lse_bytes, o, qo_bytes) || overlaps(workspace, need, o, qo_bytes) ||
       overlaps(workspace, need, lse, lse_bytes) || overlaps(workspace, need, q, qo_bytes))
     return fail(FA_ERR_INVALID_ARG, "outputs or workspace alias inputs or each other");
+  // every argument checked: only now the static array's address (the one
+  // device call before the launch)
+  if (scratch && need > 0) {
+    const hipError_t e = fa::decode_scratch(&workspace, &workspace_bytes);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "no address for the static scratch array: %s", hipGetErrorString(e));
+  }
 
   const DecodeLayout lay = decode_layout(B, Hq, Hkv, d, max_seqlen_k);
   float* part_o = lay.ranges > 0 ? static_cast<float*>(workspace) : nullptr;
@@ -228,6 +244,23 @@ FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_c
   const hipError_t e = fa::launch_decode_bf16(a);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+FA_EXPORT fa_status_t fa_decode(fa_dtype_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cu_seqlens_k, int max_seqlen_k, void* o, float* lse, int B,
+                                int Hq, int Hkv, int d, float scale, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_impl(dtype, q, k_cache, v_cache, cu_seqlens_k, max_seqlen_k, o, lse, B, Hq, Hkv, d, scale, workspace,
+                     workspace_bytes, stream, false);
+}
+
+FA_EXPORT fa_status_t fa_decode_noalloc(fa_dtype_t dtype, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* cu_seqlens_k, int max_seqlen_k, void* o, float* lse, int B,
+                                        int Hq, int Hkv, int d, float scale, void* stream) {
+  return decode_impl(dtype, q, k_cache, v_cache, cu_seqlens_k, max_seqlen_k, o, lse, B, Hq, Hkv, d, scale, nullptr, 0,
+                     stream, true);
 }
 
 namespace {

@@ -49,10 +49,44 @@
 // tiles as its units, so that every tile lies inside one block and its rows
 // are found with one table lookup (a scalar load) per tile.  The combine is
 // the same, over tile units.
+#include <mutex>
+
+#include "fa.h"
 #include "fa_common.h"
 #include "fa_kernels.h"
 
+// Partial results of fa_decode_noalloc: a static array on every device the
+// library runs on, for callers that cannot allocate.  In host code the name
+// stands for a host-side shadow, not a device address: host code uses only the
+// address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[FA_DECODE_SCRATCH_BYTES];
+
 namespace fa {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices];   // per device, set on its first lookup
+}  // namespace
+
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_addr[dev] = p;
+  }
+  *ptr = scratch_addr[dev];
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
+
 namespace {
 
 // Cache rows are read once per call and the cache is far larger than the

@@ -77,6 +77,10 @@ hipError_t launch_decode_bf16(const DecodeArgs& a);
 hipError_t launch_decode_paged_bf16(const DecodeArgs& a);
 
 int decode_max_group();       // largest Hq/Hkv the decode kernel handles
+
+// Device address (valid on the current device) and size of the decode
+// kernels' static scratch array; the address is looked up once per device.
+hipError_t decode_scratch(void** ptr, size_t* bytes);
 constexpr int kDecodeTile = 32;   // keys per decode tile (paged blocks hold whole tiles)
 
 }  // namespace fa

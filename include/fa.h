@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
     FA_OK = 0,
@@ -163,6 +163,33 @@ fa_status_t fa_decode(fa_dtype_t dtype,
 
 /* Bytes of workspace fa_decode needs for these sizes (0 when no work). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_seqlen_k);
+
+/* fa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, layouts, preconditions, results and errors as fa_decode,
+ * without the workspace: the partial results live in a static device array of
+ * FA_DECODE_SCRATCH_BYTES bytes that the library holds on every GPU it runs
+ * on until the process ends (its address is looked up once per device, on the
+ * first call with that device current).  The call allocates nothing and frees
+ * nothing.  Returns FA_ERR_WORKSPACE when fa_decode_workspace_bytes(B, Hq,
+ * Hkv, d, max_seqlen_k) exceeds FA_DECODE_SCRATCH_BYTES (the varlen decode of
+ * 32 sequences, Hq 64, Hkv 8, d 128, caches up to 32768 rows needs about
+ * 9.5 MB), and FA_ERR_HIP when the array's address cannot be obtained.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (no part of it needs to start at zero: every partial result read is
+ * written by the same call first).  Calls that overlap on one GPU -- on
+ * different streams, or from different threads without ordering -- race on
+ * the array; order them on one stream.
+ */
+#define FA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+
+fa_status_t fa_decode_noalloc(fa_dtype_t dtype,
+                              const void *q, const void *k_cache, const void *v_cache,
+                              const int32_t *cu_seqlens_k, int max_seqlen_k,
+                              void *o, float *lse,
+                              int B, int Hq, int Hkv, int d, float scale, void *stream);
 
 /* Decode on a paged KV cache, with the new token's K/V row appended first.
  *

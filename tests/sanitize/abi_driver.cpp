@@ -23,6 +23,11 @@ hipError_t launch_bwd_bf16(const BwdArgs&) { ++launches; return hipSuccess; }
 hipError_t launch_decode_bf16(const DecodeArgs& a) { ++launches; last_decode = a; return hipSuccess; }
 hipError_t launch_decode_paged_bf16(const DecodeArgs& a) { ++launches; last_decode = a; return hipSuccess; }
 int decode_max_group() { return 16; }
+hipError_t decode_scratch(void** ptr, size_t* bytes) {
+  *ptr = reinterpret_cast<void*>((uintptr_t)0x7000000000ull);
+  *bytes = FA_DECODE_SCRATCH_BYTES;
+  return hipSuccess;
+}
 }  // namespace fa
 extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
 
@@ -92,6 +97,19 @@ int main() {
          FA_ERR_UNSUPPORTED, "decode group of 32");
   expect((int)fa_decode(FA_BF16, P(1), P(2), P(3), I(6), L, P(4), F(5), B, Hq, Hkv, d, 0.1f, P(4), ws, nullptr),
          FA_ERR_INVALID_ARG, "decode workspace aliases o");
+
+  // ---- fa_decode_noalloc: the partial results go to the static array
+  before = launches;
+  expect((int)fa_decode_noalloc(FA_BF16, P(1), P(2), P(3), I(6), L, P(4), F(5), B, Hq, Hkv, d, 0.1f, nullptr), FA_OK,
+         "noalloc valid");
+  if (launches != before + 1 || (uintptr_t)last_decode.part_o != 0x7000000000ull) ++failures;
+  expect((int)fa_decode_noalloc(FA_BF16, P(1), P(2), P(3), I(6), 1 << 22, P(4), F(5), 64, 64, 1, d, 0.1f, nullptr),
+         FA_ERR_UNSUPPORTED, "noalloc group of 64");
+  expect((int)fa_decode_noalloc(FA_BF16, P(1), P(2), P(3), I(6), 1 << 22, P(4), F(5), 1024, 16, 1, d, 0.1f, nullptr),
+         FA_ERR_WORKSPACE, "noalloc beyond the static array");
+  expect((int)fa_decode_noalloc(FA_BF16, P(1), P(2), P(3), I(6), L, P(1), F(5), B, Hq, Hkv, d, 0.1f, nullptr),
+         FA_ERR_INVALID_ARG, "noalloc o aliases q");
+  if (launches != before + 1) ++failures;
 
   // ---- fa_decode_paged
   const size_t pws = fa_decode_paged_workspace_bytes(B, Hq, Hkv, d, L);

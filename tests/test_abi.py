@@ -32,7 +32,8 @@ def _no_gpu():
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
-    for n in ("fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_paged",
+    for n in ("fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_workspace_bytes", "fa_decode_noalloc",
+              "fa_decode_paged",
               "fa_decode_paged_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str",
               "fa_last_error", "fa_abi_version"):
         assert n in names
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(fa_lib):
 
 
 def test_abi_version_and_status_names(fa_lib):
-    assert fa_lib.fa_abi_version() == 4
+    assert fa_lib.fa_abi_version() == 5
     names = [fa_lib.fa_status_str(s).decode() for s in range(5)]
     assert names == ["FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE",
                      "FA_ERR_HIP"]
@@ -361,3 +362,20 @@ def test_bwd_alignment_aliasing_and_workspace(fa_lib):
     assert call(dk=dv) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
     assert call(ws=do) == FA_ERR_INVALID_ARG and "alias" in fa_lib.fa_last_error().decode()
     assert call(ws_bytes=need - 1) == FA_ERR_WORKSPACE
+
+
+
+def test_decode_noalloc_refuses_before_touching_the_device(fa_lib):
+    """fa_decode_noalloc checks its arguments like fa_decode, and refuses sizes
+    whose partial results exceed the static array, before any device call."""
+    call = lambda B, Hq, Hkv, L, d=128, o=0x100000: fa_lib.fa_decode_noalloc(
+        BF16, 0x200000, 0x300000, 0x400000, 0x500000, L, o, 0x600000, B, Hq, Hkv, d, 0.1, None)
+    assert call(1024, 16, 1, 1 << 22) == FA_ERR_WORKSPACE
+    assert b"static array" in fa_lib.fa_last_error()
+    assert call(4, 64, 1, 1000) == FA_ERR_UNSUPPORTED                 # group of 64 query heads
+    assert call(4, 8, 2, 1000, d=96) == FA_ERR_UNSUPPORTED
+    assert call(-1, 8, 2, 1000) == FA_ERR_INVALID_ARG
+    assert call(4, 8, 2, 1000, o=0x200000) == FA_ERR_INVALID_ARG      # o aliases q
+    assert call(0, 8, 2, 1000) == FA_OK                               # no work, no device call
+    # the decode workload fits: 32 sequences, Hq 64, Hkv 8, d 128, caches up to 32768 rows
+    assert binding.decode_workspace_bytes(32, 64, 8, 128, 32768) <= binding.DECODE_SCRATCH_BYTES

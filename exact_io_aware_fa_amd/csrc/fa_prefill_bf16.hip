@@ -14,6 +14,8 @@
 // gfx950 mapping
 //  * workgroup = 8 waves = 384 query rows of one (batch, query head); wave w
 //    owns rows 48w..48w+47 as three 16-row blocks.  A KV tile is 32 keys.
+//    At head dim 64 (outside long causal launches) the workgroup is 256 rows,
+//    32 per wave, which fits two workgroups per CU.
 //    Every K and V operand a wave reads from LDS feeds the MFMAs of its three
 //    row blocks, and a copied tile serves 384 rows.  On this chip a wave's
 //    MFMAs and another wave's softmax (exponentials above all) barely overlap
@@ -61,12 +63,14 @@
 namespace fa {
 namespace {
 
-constexpr int kRows = 48;           // query rows per wave (three 16-row blocks)
-constexpr int kRB = kRows / 16;
 constexpr int kWaves = 8;
-constexpr int kBR = kRows * kWaves; // query rows per workgroup
 constexpr int kBC = 32;             // keys per KV tile
 constexpr int kThreads = kWaves * 64;
+// Query rows per wave, RW: 48 (three 16-row blocks, one workgroup per CU) or,
+// at head dim 64, 32 (two blocks; at most 128 VGPRs, so two workgroups share a
+// CU and short sequences run in one round of resident workgroups).
+template <int D, int RW>
+constexpr int waves_per_eu() { return RW == 32 ? 4 : 2; }
 // Weights may exceed 1 by up to 2^kRescaleSlack before O is rescaled: fp32
 // sums and bf16 weights hold that exactly in range, and the rescale (vector
 // work on all accumulators) then happens only for an extreme jump of the max.
@@ -99,11 +103,15 @@ __device__ __forceinline__ int swz_v(int row) {
 // VARLEN: q/o are packed [total_q, Hq, d] and k/v [total_k, Hkv, d], sequence
 // b owning rows cu_q[b]..cu_q[b+1]-1 and cu_k[b]..cu_k[b+1]-1; LSE is
 // [Hq, total_q].  N_arg / Nk_arg are then upper bounds that size the grid.
-template <int D, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
+template <int D, bool CAUSAL, bool VARLEN, int RW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_eu<D, RW>())))
+void prefill_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int N_arg, int Nk_arg, int Hq, int Hkv, float c,
     int n_qtiles, int n_work, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int total_q) {
+  constexpr int kRows = RW;                 // query rows per wave
+  constexpr int kRB = kRows / 16;           // 16-row blocks per wave
+  constexpr int kBR = kRows * kWaves;       // query rows per workgroup
   constexpr int DT = D / 32;                // MFMA k-steps of S^T = K Q^T (32 head-dim values each)
   constexpr int DB = D / 16;                // 16-wide head-dim blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -554,23 +562,34 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool VARLEN>
+template <int D, bool CAUSAL, bool VARLEN, int RW>
 hipError_t launch(const PrefillArgs& a) {
+  constexpr int kBR = RW * kWaves;
   const int n_qtiles = (a.N + kBR - 1) / kBR;
   const int64_t n_work = (int64_t)a.B * a.Hq * n_qtiles;
   if (n_work == 0) return hipSuccess;
   const int64_t grid = (n_work + 7) / 8 * 8;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(kThreads), 0, a.stream,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, VARLEN, RW>), dim3((unsigned)grid), dim3(kThreads), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                      a.lse, a.N, a.Nk, a.Hq, a.Hkv, a.scale * kLog2e, n_qtiles, (int)n_work, a.cu_q, a.cu_k,
                      a.total_q);
   return hipGetLastError();
 }
 
+// Rows per wave at head dim 64.  32 (two workgroups per CU) wins wherever the
+// work is even or short: measured against 48 on one box, B16 H16 N512 44 ->
+// 29 us, causal B8 H12 N1024 47 -> 41 us, causal N2048 -23..-26%, full N1024
+// and N4096 -33% and -19%.  Causal N4096 ties, and causal B1 H16 N8192 is 19%
+// slower with 32: its one round of resident workgroups pairs the long
+// diagonal-band tiles on shared CUs, where one workgroup per CU runs them in
+// LPT order.  (N is the longest query sequence for varlen.)
 template <bool VARLEN>
 hipError_t dispatch(const PrefillArgs& a) {
-  if (a.d == 64) return a.causal ? launch<64, true, VARLEN>(a) : launch<64, false, VARLEN>(a);
-  return a.causal ? launch<128, true, VARLEN>(a) : launch<128, false, VARLEN>(a);
+  if (a.d == 64) {
+    if (!a.causal) return launch<64, false, VARLEN, 32>(a);
+    return a.N > 4096 ? launch<64, true, VARLEN, 48>(a) : launch<64, true, VARLEN, 32>(a);
+  }
+  return a.causal ? launch<128, true, VARLEN, 48>(a) : launch<128, false, VARLEN, 48>(a);
 }
 
 }  // namespace

@@ -377,9 +377,8 @@ FA_EXPORT fa_status_t fa_decode_paged(fa_dtype_t dtype, const void* q, const voi
 
 FA_EXPORT size_t fa_bwd_workspace_bytes(int B, int Hq, int N) {
   if (B <= 0 || Hq <= 0 || N <= 0) return 0;
-  // D then the base-2 LSE, [B, Hq, N] fp32 each, the second 256-byte aligned
-  const size_t one = ((size_t)B * Hq * N * sizeof(float) + 255) / 256 * 256;
-  return 2 * one;
+  // per (batch, head) and 32-row query tile: the rows' base-2 LSE, then D (fp32)
+  return (size_t)B * Hq * ((N + 31) / 32) * 64 * sizeof(float);
 }
 
 FA_EXPORT fa_status_t fa_bwd(fa_dtype_t dtype, const void* q, const void* k, const void* v, const void* o,
@@ -424,10 +423,8 @@ FA_EXPORT fa_status_t fa_bwd(fa_dtype_t dtype, const void* q, const void* k, con
       if ((spans[i].written || spans[j].written) && overlaps(spans[i].p, spans[i].n, spans[j].p, spans[j].n))
         return fail(FA_ERR_INVALID_ARG, "gradients or workspace alias other arguments");
 
-  float* dsum = static_cast<float*>(workspace);
-  float* lse2 = need > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2) : nullptr;
-  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, dsum, lse2, B, Hq, Hkv, N, Nk, d, causal != 0, scale,
-                reinterpret_cast<hipStream_t>(stream)};
+  fa::BwdArgs a{q,  k,  v,  o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv, N, Nk, d,
+                causal != 0, scale, reinterpret_cast<hipStream_t>(stream)};
   const hipError_t e = fa::launch_bwd_bf16(a);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -11,22 +11,28 @@
 // head summed into its dK and dV.
 //
 // Three kernels, no atomics (each output row has one owner):
-//  * bwd_pre_kernel: D and the base-2 LSE (+inf for a row without keys, so
-//    that its P is 0) per (batch, head, row), into the workspace;
+//  * bwd_pre_kernel: per 32-row query tile of each (batch, head), the rows'
+//    base-2 LSE (+inf for a row without keys or past N, so that its P is 0)
+//    and D, into the workspace;
 //  * bwd_dq_kernel: one workgroup per (query tile, query head, batch),
 //    streaming K/V tiles: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T;
 //  * bwd_dkdv_kernel: one workgroup per (key tile, kv head, batch), streaming
-//    the Q and dO tiles of the group's query heads: S = Q K^T, dP = dO V^T,
-//    dV^T += dO^T P, dK^T += Q^T dS.
+//    the Q and dO tiles of the group's query heads; pairs of waves share 32
+//    keys, one computing S = Q K^T, P and dV^T += dO^T P, the other, a tile
+//    behind, dP = dO V^T, dS and dK^T += Q^T dS.
 // Both use the forward's MFMA layout: with the streamed operand's rows fed in
 // the permuted order pi16, a lane of a 16x16x32 result holds 8 consecutive
 // entries of one row of P or dS, which is exactly its slice of the next
-// product's B operand, so P and dS never leave registers.  The second
-// operand of each product is either held in registers for the whole loop (Q
-// and dO in bwd_dq, K and V in bwd_dkdv) or read from the streamed LDS tile:
-// by rows (ds_read_b128) as an A operand, or transposed (ds_read_b64_tr_b16)
-// as the A operand of a transposed product.  S and dP are computed in both
-// kernels: 7 matrix products in all, against 5 with atomics on dQ.
+// product's B operand, so P and dS stay in registers (bwd_dkdv hands P from
+// one wave of a pair to the other through LDS in that same lane order).  The
+// second operand of each product is either held in registers for the whole
+// loop (Q and dO in bwd_dq, K or V in bwd_dkdv) or read from the streamed LDS
+// tile: by rows (ds_read_b128) as an A operand, or transposed
+// (ds_read_b64_tr_b16) as the A operand of a transposed product.  S and dP
+// are computed in both kernels: 7 matrix products in all, against 5 with
+// atomics on dQ.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -60,20 +66,26 @@ __device__ __forceinline__ int swz(int row) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// ---- D_i = dO_i . O_i and lse2_i = LSE_i log2(e) (+inf when LSE_i = -inf),
-// both [B, Hq, N]; D/8 lanes per (b, i, h) row of the BSHD tensors.
+// ---- The workspace ld [B*Hq][ntq][2*kT], ntq = ceil(N / kT): for query tile
+// t of (batch, head), lse2 of its rows (LSE log2(e); +inf for LSE = -inf and
+// for rows past N) then their D_i = dO_i . O_i (0 past N).  D/8 lanes per row.
 template <int D>
 __global__ __launch_bounds__(kThr) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
-                                                       const float* __restrict__ lse, float* __restrict__ dsum,
-                                                       float* __restrict__ lse2, int B, int N, int Hq) {
+                                                       const float* __restrict__ lse, float* __restrict__ ld, int B,
+                                                       int N, int Hq, int ntq) {
   constexpr int LPR = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * kThr + threadIdx.x;
-  const int64_t row = gid / LPR;
+  const int64_t prow = gid / LPR;                    // row of the padded [B*Hq][ntq*kT] range
   const int part = (int)(gid % LPR);
-  const int64_t nrows = (int64_t)B * N * Hq;
+  const int64_t per_bh = (int64_t)ntq * kT;
+  const int64_t bh = prow / per_bh;
+  const int i = (int)(prow - bh * per_bh);
+  const bool valid = bh < (int64_t)B * Hq;
+  const bool in = valid && i < N;
   float acc = 0.0f;
-  if (row < nrows) {
+  if (in) {
+    const int64_t row = ((bh / Hq) * N + i) * Hq + bh % Hq;
     const u32x4 a = load16(o + row * D + part * 8);
     const u32x4 g = load16(dout + row * D + part * 8);
 #pragma unroll
@@ -81,15 +93,11 @@ __global__ __launch_bounds__(kThr) void bwd_pre_kernel(const uint16_t* __restric
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < nrows && part == 0) {
-    const int h = (int)(row % Hq);
-    const int64_t bi = row / Hq;
-    const int i = (int)(bi % N);
-    const int64_t b = bi / N;
-    const int64_t idx = (b * Hq + h) * N + i;
-    dsum[idx] = acc;
-    const float l = lse[idx];
-    lse2[idx] = l == -INFINITY ? INFINITY : l * kLog2e;
+  if (valid && part == 0) {
+    float* blk = ld + (bh * ntq + i / kT) * (2 * kT);
+    const float l = in ? lse[bh * N + i] : -INFINITY;
+    blk[i % kT] = l == -INFINITY ? INFINITY : l * kLog2e;
+    blk[kT + i % kT] = acc;
   }
 }
 
@@ -128,8 +136,8 @@ struct TileCopy {
 template <int D, bool CAUSAL, int WQ, int RB>
 __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
-    uint16_t* __restrict__ dq, int N, int Nk, int Hq, int Hkv, float c, float scale, int n_qtiles, int n_work) {
+    const uint16_t* __restrict__ dout, const float* __restrict__ ld, uint16_t* __restrict__ dq, int N, int Nk,
+    int Hq, int Hkv, float c, float scale, int ntq, int n_qtiles, int n_work) {
   static_assert(WQ * 64 >= kThr, "staging copies use the first 256 threads");
   constexpr int DT = D / 32, DB = D / 16, CPR = D / 8;
   constexpr int ROWS_W = 16 * RB, ROWS_G = ROWS_W * WQ;
@@ -175,9 +183,10 @@ __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
       df[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(d_rsrc, off + t * 64));
     }
     const bool in = row >= 0 && row < N;
-    const int64_t li = ((int64_t)b * Hq + h) * N + (in ? row : 0);
-    l2[rb] = in ? lse2[li] : INFINITY;                // P = 0 for absent rows
-    ds[rb] = in ? dsum[li] : 0.0f;
+    const int ri = in ? row : 0;
+    const int64_t li = ((int64_t)(b * Hq + h) * ntq + ri / kT) * (2 * kT) + ri % kT;
+    l2[rb] = in ? ld[li] : INFINITY;                  // P = 0 for absent rows
+    ds[rb] = in ? ld[li + kT] : 0.0f;
   }
 
   // key tiles this workgroup needs; tiles below n_clean need no mask for this wave
@@ -317,29 +326,76 @@ __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
   }
 }
 
-#ifndef BWD_OCC
-#define BWD_OCC 1
+// ---- dK and dV.  Workgroup: 8 waves over 128 keys of one kv head, as 4 pairs
+// of waves on 32 keys each; the two waves of a pair (waves p and p + 4) run
+// on one SIMD.  It streams the 32-row Q and dO tiles of every query head of
+// the group, from the last query tile down to the first that sees one of its
+// keys, heads innermost: the workgroups of one kv head start on the same tile
+// and move through the tiles together, so they share each one in L2.
+// Per tile, wave A of a pair computes S = Q K^T, P (masked) and
+// dV^T += dO^T P, and leaves P (fp32) in LDS; wave B, one tile behind,
+// computes dP = dO V^T, dS = P o (dP - D) and dK^T += Q^T dS.  Both do the
+// same number of MFMAs per tile, and one's exponentials or dS arithmetic run
+// beside the other's products.  The tiles, with lse2 and D of their rows,
+// reach LDS by buffer_load ... lds through a ring of 4 stages, two tiles
+// ahead; one workgroup barrier per tile.
+constexpr int kDkWaves = 8;                         // 4 pairs
+constexpr int kDkRB = 2;                            // 16-key blocks per pair
+constexpr int kDkKeys = 16 * kDkRB * kDkWaves / 2;  // keys per workgroup
+#ifndef BWD_DK_NS
+#define BWD_DK_NS 4
 #endif
-#ifndef BWD_RA
-#define BWD_RA 2
-#endif
+constexpr int kDkNS = BWD_DK_NS;                    // stages of the Q/dO ring (copies run kDkNS - 2 tiles ahead)
+static_assert(kDkNS == 4 || kDkNS == 6, "ring of 4 or 6 stages (an even count keeps the P buffer static)");
 
-
-// ---- dK and dV.  Workgroup: WK waves x (16 RB) keys of one kv head; it
-// streams 32-row Q and dO tiles (with their lse2 and D) of every query head
-// of the group, from the first query tile that sees one of its keys.
-template <int D, bool CAUSAL, int WK, int RB>
-__global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ dsum,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int Nk, int Hq, int Hkv, float c, float scale,
-    int n_ktiles, int n_work) {
-  constexpr int DT = D / 32, DB = D / 16, CPR = D / 8;
-  constexpr int KEYS_W = 16 * RB, KEYS_G = KEYS_W * WK;
-  __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][kT * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t sO[2][kT * D];
-  __shared__ __attribute__((aligned(16))) float sL[2][kT];
-  __shared__ __attribute__((aligned(16))) float sD[2][kT];
+    const uint16_t* __restrict__ dout, const float* __restrict__ ld, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int N, int Nk, int Hq, int Hkv, float c, float scale, int ntq, int n_ktiles,
+    int n_work) {
+  constexpr int DT = D / 32, DB = D / 16, CPR = D / 8, RB = kDkRB;
+  constexpr int TILE_BYTES = kT * D * 2;            // one tensor's tile
+  constexpr int INSTR_T = TILE_BYTES / 1024;        // 1 KB copies per tensor tile
+  constexpr int DMA_PW = 2 * INSTR_T / kDkWaves;    // tile copies per wave
+  constexpr int RPI = 1024 / (2 * D);               // rows per copy
+  constexpr int LD_PW = 2 * kT * 4 / kDkWaves;      // bytes of lse2/D per wave (2 lanes x 16)
+  static_assert(DMA_PW >= 1 && 2 * INSTR_T == DMA_PW * kDkWaves && INSTR_T % DMA_PW == 0,
+                "each wave copies whole 1 KB blocks of one tensor");
+  static_assert(LD_PW == 32, "two 16-byte lanes of lse2/D per wave");
+  // One LDS variable per stage and buffer: the compiler keeps apart the
+  // accesses it can attribute to different variables, so a copy in flight
+  // into one stage does not make it wait before reads of another (the step
+  // loop below is unrolled by 4 so that every stage is named statically).
+  __shared__ __attribute__((aligned(1024))) char sQ0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sQ1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sQ2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sQ3[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sQ4[kDkNS > 4 ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char sQ5[kDkNS > 4 ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char sO0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO3[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO4[kDkNS > 4 ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char sO5[kDkNS > 4 ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(256))) float sL0[2 * kT];   // lse2[kT], D[kT]
+  __shared__ __attribute__((aligned(256))) float sL1[2 * kT];
+  __shared__ __attribute__((aligned(256))) float sL2[2 * kT];
+  __shared__ __attribute__((aligned(256))) float sL3[2 * kT];
+  __shared__ __attribute__((aligned(256))) float sL4[kDkNS > 4 ? 2 * kT : 4];
+  __shared__ __attribute__((aligned(256))) float sL5[kDkNS > 4 ? 2 * kT : 4];
+  __shared__ __attribute__((aligned(1024))) f32x4 sP0[kDkWaves / 2][RB][2][64];   // P of a pair, by lane
+  __shared__ __attribute__((aligned(1024))) f32x4 sP1[kDkWaves / 2][RB][2][64];
+  auto qS = [&](const int st) -> char* {
+    return st == 0 ? sQ0 : st == 1 ? sQ1 : st == 2 ? sQ2 : st == 3 ? sQ3 : st == 4 ? sQ4 : sQ5;
+  };
+  auto oS = [&](const int st) -> char* {
+    return st == 0 ? sO0 : st == 1 ? sO1 : st == 2 ? sO2 : st == 3 ? sO3 : st == 4 ? sO4 : sO5;
+  };
+  auto lS = [&](const int st) -> float* {
+    return st == 0 ? sL0 : st == 1 ? sL1 : st == 2 ? sL2 : st == 3 ? sL3 : st == 4 ? sL4 : sL5;
+  };
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   if (logical >= n_work) return;
@@ -350,46 +406,69 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
   rest /= n_ktiles;
   const int b = rest % n_batch;
   const int g = rest / n_batch;
-  const int k0 = krank * KEYS_G;
+  const int k0 = krank * kDkKeys;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int kw = k0 + KEYS_W * wave;
+  const int pair = wave % (kDkWaves / 2);
+  const int role = wave / (kDkWaves / 2);           // 0: S, P, dV;  1: dP, dS, dK
+  const int kp = k0 + 16 * RB * pair;               // the pair's first key
   const int offs = Nk - N;
 
-  // K and V rows -> B operands (lane (key j, group c): head-dim 32t + 8c..);
-  // keys past Nk read 0 (their dK and dV are not stored)
+  // K (role 0) or V (role 1) rows -> B operands: lane (key j, group c) holds
+  // head-dim 32t + 8c..; keys past Nk read 0 (their dK and dV are not stored)
   const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 2;
   const int64_t ks = ((int64_t)b * Nk * Hkv + g) * D;
   const uint32_t kv_bytes = (uint32_t)((Nk - 1) * Hkv + 1) * D * 2;
-  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(k + ks, kv_bytes);
-  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(v + ks, kv_bytes);
-  bf16x8 kf[RB][DT], vf[RB][DT];
+  const __amdgpu_buffer_rsrc_t kv_rsrc = make_rsrc((role == 0 ? k : v) + ks, kv_bytes);
+  bf16x8 kvf[RB][DT];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const uint32_t off = (uint32_t)(kw + 16 * rb + l16) * kv_row_bytes + grp * 16;
+    const uint32_t off = (uint32_t)(kp + 16 * rb + l16) * kv_row_bytes + grp * 16;
 #pragma unroll
-    for (int t = 0; t < DT; ++t) {
-      kf[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(k_rsrc, off + t * 64));
-      vf[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(v_rsrc, off + t * 64));
-    }
+    for (int t = 0; t < DT; ++t) kvf[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(kv_rsrc, off + t * 64));
   }
 
-  // query tiles: causal rows i see key j iff j <= i + offs, so this
-  // workgroup's keys are seen from row k0 - offs on
-  const int nq = (N + kT - 1) / kT;
-  const int qt0 = CAUSAL ? min(nq, max(0, k0 - offs) / kT) : 0;
-  const int per_head = nq - qt0;
-  const int n_it = G * per_head;
-  // the tile at row i0 needs a mask for this wave iff some key of the wave
-  // is invisible to its first row: i0 + offs < kw + KEYS_W - 1
+  // query tiles: causal row i sees key j iff j <= i + offs, so the
+  // workgroup's keys are seen from row k0 - offs on.  Iteration `it` takes
+  // tile ntq - 1 - it / G of query head g*G + it % G.
+  const int qt0 = CAUSAL ? min(ntq, max(0, k0 - offs) / kT) : 0;
+  const int n_it = G * (ntq - qt0);
 
+  // ---- copies: wave w moves 1 KB blocks w*DMA_PW.. of the stage's [Q, dO]
+  // pair (lane l of a block fills row blk*RPI + l/CPR, physical chunk l%CPR),
+  // all of one tensor, and with lanes 0-1 bytes 32w..32w+31 of the tile's
+  // lse2/D block.  Every wave issues DMA_PW + 1 copies per tile.
+  const int dma_t = wave * DMA_PW / INSTR_T;         // 0: Q, 1: dO
   const uint32_t q_row_bytes = (uint32_t)Hq * D * 2;
-  // (N = 0: no query tile is loaded, n_it = 0; the view is then empty)
-  const uint32_t q_bytes = N > 0 ? (uint32_t)((N - 1) * Hq + 1) * D * 2 : 0u;
-  auto head_rsrc = [&](const uint16_t* base, int h) {
-    return make_rsrc(base + ((int64_t)b * N * Hq + h) * D, q_bytes);
+  const uint16_t* src = (dma_t == 0 ? q : dout) + (int64_t)b * N * Hq * D;
+  uint32_t voff[DMA_PW];
+#pragma unroll
+  for (int i = 0; i < DMA_PW; ++i) {
+    const int row = ((wave * DMA_PW + i) % INSTR_T) * RPI + lane / CPR;
+    voff[i] = (uint32_t)row * q_row_bytes + (uint32_t)(((lane % CPR) ^ swz<CPR>(row)) * 16);
+  }
+  const uint32_t ld_voff = (uint32_t)(LD_PW * wave + 16 * lane);
+  // Every call issues the same copies: for an iteration past the last, the
+  // views are empty, so the copies write zeros into a free stage and read
+  // nothing; the waits below count copies.
+  auto issue = [&](const int it, const int st) __attribute__((always_inline)) {
+    const bool real = it < n_it;
+    const int ti = real ? ntq - 1 - it / G : 0;
+    const int h = g * G + (real ? it % G : 0);
+    const int i0 = ti * kT;
+    // view: row i0 of head h to the end of the slice (rows past N read 0)
+    const uint32_t bytes = real ? (uint32_t)((N - 1 - i0) * Hq + 1) * D * 2 : 0u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + ((int64_t)i0 * Hq + h) * D, bytes);
+    char* dst = dma_t == 0 ? qS(st) : oS(st);
+#pragma unroll
+    for (int i = 0; i < DMA_PW; ++i)
+      buffer_load16_to_lds(r, voff[i], 0, (lds_void*)(dst + ((wave * DMA_PW + i) % INSTR_T) * 1024));
+    const __amdgpu_buffer_rsrc_t rl =
+        make_rsrc(ld + ((int64_t)(b * Hq + h) * ntq + ti) * (2 * kT), real ? 2 * kT * 4 : 0);
+    if (lane < 2)
+      buffer_load16_to_lds(rl, ld_voff, 0, (lds_void*)(reinterpret_cast<char*>(lS(st)) + LD_PW * wave));
   };
 
   int r_off[2][DT];
@@ -407,171 +486,185 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
     t_off[db] = trow * (2 * D) + ((chunk ^ swz<CPR>(trow)) * 16) + (l16 & 1) * 8;
   }
 
-  f32x4 acc_k[RB][DB], acc_v[RB][DB];   // dK^T, dV^T: lane (key j, group c) item r = head-dim 16db + 4c + r
+  f32x4 acc[RB][DB];   // dV^T (role 0) or dK^T (role 1): lane (key j, group c) item r = head-dim 16db + 4c + r
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int db = 0; db < DB; ++db) acc_k[rb][db] = acc_v[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Staging of iteration `it`: Q and dO tiles of head g*G + it/per_head,
-  // rows (qt0 + it%per_head)*32..; lse2 (+inf past N) and D for those rows.
-  // Their loads mostly miss L2, so they run two tiles ahead: two register
-  // sets, tile t in set t % 2; the loads of tile it+2 are issued at the start
-  // of iteration it, and tile it+1 is stored to LDS at its end.  (A third set
-  // makes the unrolled loop spill at d=128.)  CT threads copy: one 16-byte
-  // chunk each per tensor at d=128 with 8 waves.
-  constexpr int CT = 64 * WK < kT * CPR ? 64 * WK : kT * CPR;
-  struct Stage {
-    TileCopy<D, CT> cq, co;
-    float l = INFINITY, d = 0.0f;
+  // The two products of a tile: mm1 computes S = Q K^T (wave A, `rows` = Q)
+  // or dP = dO V^T (wave B, `rows` = dO) into x; mm2 adds dO^T P (wave A)
+  // or Q^T dS (wave B) to acc, wf holding P or dS as B operands and trf the
+  // transposed reads of dO or Q (fetched by prefetch_tr).  x: lane (key j,
+  // group c) item r of block kb = query 8c + 4kb + r of the tile.
+  f32x4 x[RB][2];
+  bf16x8 wf[RB];
+  bf16x8 trf[DB];
+  bf16x8 ra[2][DT];
+  auto read_rows = [&](const char* rows) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < DT; ++t) ra[kb][t] = __builtin_bit_cast(bf16x8, load16(rows + r_off[kb][t]));
   };
-  Stage st0, st1;
-  auto load_it = [&](const int it, Stage& st) {
-    const int h = g * G + it / per_head;
-    const int i0 = (qt0 + it % per_head) * kT;
-    if (tid < CT) {
-      st.cq.load(head_rsrc(q, h), i0, q_row_bytes, tid);
-      st.co.load(head_rsrc(dout, h), i0, q_row_bytes, tid);
-    }
-    if (tid < kT) {
-      const int row = i0 + tid;
-      const int64_t li = ((int64_t)b * Hq + h) * N + (row < N ? row : 0);
-      st.l = row < N ? lse2[li] : INFINITY;
-      st.d = row < N ? dsum[li] : 0.0f;
-    }
-  };
-  auto store_it = [&](const int buf, const Stage& st) {
-    if (tid < CT) {
-      st.cq.store(reinterpret_cast<char*>(sQ[buf]), tid);
-      st.co.store(reinterpret_cast<char*>(sO[buf]), tid);
-    }
-    if (tid < kT) {
-      sL[buf][tid] = st.l;
-      sD[buf][tid] = st.d;
-    }
-  };
-
-  if (n_it > 0) {
-    load_it(0, st0);
-    if (n_it > 1) load_it(1, st1);
-    store_it(0, st0);
-    __syncthreads();
-  }
-  // iteration `it`: `ld` receives tile it+2, `nx` holds tile it+1
-  auto step = [&](const int it, Stage& ld, Stage& nx) __attribute__((always_inline)) {
-    if (it + 2 < n_it) load_it(it + 2, ld);
-    const int i0 = (qt0 + it % per_head) * kT;
-    const char* qt = reinterpret_cast<const char*>(sQ[it & 1]);
-    const char* ot = reinterpret_cast<const char*>(sO[it & 1]);
-    // S = Q K^T and dP = dO V^T: lane (key j, group c) item r of block kb =
-    // query 8c + 4kb + r of the tile
-    f32x4 s[RB][2], dp[RB][2];
+  auto mm1 = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[rb][kb] = dp[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) x[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const bf16x8 qa = __builtin_bit_cast(bf16x8, load16(qt + r_off[kb][t]));
-        const bf16x8 oa = __builtin_bit_cast(bf16x8, load16(ot + r_off[kb][t]));
+      for (int t = 0; t < DT; ++t)
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          s[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, kf[rb][t], s[rb][kb], 0, 0, 0);
-          dp[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, vf[rb][t], dp[rb][kb], 0, 0, 0);
-        }
-      }
+        for (int rb = 0; rb < RB; ++rb)
+          x[rb][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ra[kb][t], kvf[rb][t], x[rb][kb], 0, 0, 0);
     }
-    // LDS reads run BWD_RA steps ahead of the MFMAs that use them
-    if constexpr (BWD_RA > 0) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * BWD_RA, 0);
+  };
+  auto prefetch_tr = [&](const char* trs) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 2 * DT; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
-      }
+    for (int db = 0; db < DB; ++db) {
+      const u32x2 lo = lds_read_tr16(trs + t_off[db]);
+      const u32x2 hi = lds_read_tr16(trs + t_off[db] + 4 * (2 * D));
+      trf[db] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
-    // lse2 and D of this lane's 8 queries (8c..8c+7)
-    const f32x4 la = *reinterpret_cast<const f32x4*>(&sL[it & 1][8 * grp]);
-    const f32x4 lb = *reinterpret_cast<const f32x4*>(&sL[it & 1][8 * grp + 4]);
-    const f32x4 da = *reinterpret_cast<const f32x4*>(&sD[it & 1][8 * grp]);
-    const f32x4 dbv = *reinterpret_cast<const f32x4*>(&sD[it & 1][8 * grp + 4]);
-    const bool masked = CAUSAL && i0 + offs < kw + KEYS_W - 1;
-    bf16x8 pf[RB], dsf[RB];
+  };
+  auto mm2 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(trf[db], wf[rb], acc[rb][db], 0, 0, 0);
+  };
+  auto pack = [&](float (*w)[8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      float p[8], e[8];
+      const u32x4 u = {pack_bf16x2(w[rb][0], w[rb][1]), pack_bf16x2(w[rb][2], w[rb][3]),
+                       pack_bf16x2(w[rb][4], w[rb][5]), pack_bf16x2(w[rb][6], w[rb][7])};
+      wf[rb] = __builtin_bit_cast(bf16x8, u);
+    }
+  };
+  // wave A: P = 2^(s c - lse2) of iteration `it` (0 where masked; key
+  // kp + 16rb + l16 is visible to query i0 + 8c + i iff key <= i0 + 8c + i +
+  // offs), into wf and, in fp32, into the pair's slot of `pbuf`
+  auto soft_a = [&](const int it, const float* ldv, f32x4 (*pbuf)[RB][2][64]) __attribute__((always_inline)) {
+    const int i0 = (ntq - 1 - it / G) * kT;
+    const f32x4 la = *reinterpret_cast<const f32x4*>(&ldv[8 * grp]);
+    const f32x4 lb = *reinterpret_cast<const f32x4*>(&ldv[8 * grp + 4]);
+    const bool masked = CAUSAL && i0 + offs < kp + 16 * RB - 1;
+    f32x4* pslot = &pbuf[pair][0][0][lane];        // [rb][half] at stride 64
+    float w[RB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float l = kb == 0 ? la[r] : lb[r];
-          const float dd = kb == 0 ? da[r] : dbv[r];
-          p[4 * kb + r] = fast_exp2(fmaf(s[rb][kb][r], c, -l));
-          e[4 * kb + r] = p[4 * kb + r] * (dp[rb][kb][r] - dd);
-        }
+        for (int r = 0; r < 4; ++r) w[rb][4 * kb + r] = fast_exp2(fmaf(x[rb][kb][r], c, -(kb == 0 ? la[r] : lb[r])));
       if (masked) {
-        // key kw + 16rb + l16 is visible to query i0 + 8c + i iff key <= i0 + 8c + i + offs
-        const int rel = (i0 + 8 * grp + offs) - (kw + 16 * rb + l16);
+        const int rel = (i0 + 8 * grp + offs) - (kp + 16 * rb + l16);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = i >= -rel ? p[i] : 0.0f;
-          e[i] = i >= -rel ? e[i] : 0.0f;
-        }
+        for (int i = 0; i < 8; ++i) w[rb][i] = i >= -rel ? w[rb][i] : 0.0f;
       }
-      const u32x4 wp = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                        pack_bf16x2(p[6], p[7])};
-      const u32x4 we = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                        pack_bf16x2(e[6], e[7])};
-      pf[rb] = __builtin_bit_cast(bf16x8, wp);
-      dsf[rb] = __builtin_bit_cast(bf16x8, we);
+      pslot[128 * rb] = f32x4{w[rb][0], w[rb][1], w[rb][2], w[rb][3]};
+      pslot[128 * rb + 64] = f32x4{w[rb][4], w[rb][5], w[rb][6], w[rb][7]};
     }
-    // dV^T += dO^T P and dK^T += Q^T dS (transposed reads of the dO and Q tiles)
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const u32x2 olo = lds_read_tr16(ot + t_off[db]);
-      const u32x2 ohi = lds_read_tr16(ot + t_off[db] + 4 * (2 * D));
-      const u32x2 qlo = lds_read_tr16(qt + t_off[db]);
-      const u32x2 qhi = lds_read_tr16(qt + t_off[db] + 4 * (2 * D));
-      const bf16x8 oa = __builtin_bit_cast(bf16x8, u32x4{olo[0], olo[1], ohi[0], ohi[1]});
-      const bf16x8 qa = __builtin_bit_cast(bf16x8, u32x4{qlo[0], qlo[1], qhi[0], qhi[1]});
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        acc_v[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oa, pf[rb], acc_v[rb][db], 0, 0, 0);
-        acc_k[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, dsf[rb], acc_k[rb][db], 0, 0, 0);
-      }
-    }
-    if constexpr (BWD_RA > 0) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * BWD_RA, 0);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
-      }
-    }
-    if (it + 1 < n_it) store_it((it + 1) & 1, nx);  // last read in iteration it-1, before its barrier
-    __syncthreads();
+    pack(w);
   };
-  for (int it = 0; it < n_it; it += 2) {
-    step(it, st0, st1);
-    if (it + 1 >= n_it) break;
-    step(it + 1, st1, st0);
-  }
+  // wave B: dS = P o (dP - D), P from wave A's slot in `pbuf`
+  auto soft_b = [&](const float* ldv, f32x4 (*pbuf)[RB][2][64]) __attribute__((always_inline)) {
+    const f32x4 da = *reinterpret_cast<const f32x4*>(&ldv[kT + 8 * grp]);
+    const f32x4 dbv = *reinterpret_cast<const f32x4*>(&ldv[kT + 8 * grp + 4]);
+    const f32x4* pslot = &pbuf[pair][0][0][lane];
+    float w[RB][8];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x4 p0 = pslot[128 * rb], p1 = pslot[128 * rb + 64];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        w[rb][r] = p0[r] * (x[rb][0][r] - da[r]);
+        w[rb][4 + r] = p1[r] * (x[rb][1][r] - dbv[r]);
+      }
+    }
+    pack(w);
+  };
 
+  // Step t (ST = t % NS) has two phases; in each, one wave of a pair runs its
+  // MFMAs while the other (on the same SIMD) runs its exponentials or dS:
+  //   phase 2t:   A: dV += dO_{t-1}^T P_{t-1}, S_t = Q_t K^T  |  B: dS_{t-1}
+  //   phase 2t+1: B: dK += Q_{t-1}^T dS_{t-1}, dP_t = dO_t V^T  |  A: P_t -> LDS
+  // Tile t is read in phases 2t..2t+3; the copies of tile t+PD go out at the
+  // start of step t into the stage of tile t+PD-NS (last read in phase
+  // 2t-1).
+  constexpr int NS = kDkNS, PD = kDkNS - 2;
+  auto step = [&](const int t, const int ST) __attribute__((always_inline)) {
+    const int SB = (ST + NS - 1) % NS;              // stage of tile t-1
+    f32x4 (*p_cur)[RB][2][64] = (ST & 1) ? sP1 : sP0;
+    f32x4 (*p_prev)[RB][2][64] = (ST & 1) ? sP0 : sP1;
+    issue(t + PD, (ST + PD) % NS);
+    // (an MFMA phase issues all its LDS reads first: the transposed operands
+    // of mm2, then the rows of mm1, which land while mm2 runs)
+    if (role == 0) {
+      if (t >= 1) prefetch_tr(oS(SB));
+      if (t < n_it) read_rows(qS(ST));
+      if (t >= 1) mm2();
+      if (t < n_it) mm1();
+    } else if (t >= 1) {
+      soft_b(lS(SB), p_prev);
+    }
+    barrier_no_fence();
+    if (role == 1) {
+      if (t >= 1) prefetch_tr(qS(SB));
+      if (t < n_it) read_rows(oS(ST));
+      if (t >= 1) mm2();
+      if (t < n_it) mm1();
+    } else if (t < n_it) {
+      soft_a(t, lS(ST), p_cur);
+    }
+    wait_vmem_le<(PD - 1) * (DMA_PW + 1)>();   // tile t+1 has landed
+    barrier_no_fence();                        // ... for every wave
+  };
+
+  if (n_it > 0) {
+#pragma unroll
+    for (int t = 0; t < PD; ++t) issue(t, t);
+    wait_vmem_le<(PD - 1) * (DMA_PW + 1)>();
+    barrier_no_fence();
+    // steps 0..n_it, unrolled by NS so that every stage is named statically;
+    // the check after each step leaves the loop (it never skips ahead)
+    auto round = [&](const int s0) __attribute__((always_inline)) -> bool {
+      step(s0, 0);
+      if (s0 + 1 > n_it) return false;
+      step(s0 + 1, 1);
+      if (s0 + 2 > n_it) return false;
+      step(s0 + 2, 2);
+      if (s0 + 3 > n_it) return false;
+      step(s0 + 3, 3);
+      if (s0 + 4 > n_it) return false;
+      if constexpr (NS > 4) {
+        step(s0 + 4, 4);
+        if (s0 + 5 > n_it) return false;
+        step(s0 + 5, 5);
+        if (s0 + 6 > n_it) return false;
+      }
+      return true;
+    };
+    for (int s0 = 0; round(s0); s0 += NS) {
+    }
+  }
+  wait_vmem_all();          // no copy may land after the workgroup ends
+
+  uint16_t* dst = role == 0 ? dv : dk;
+  const float f = role == 0 ? 1.0f : scale;
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int key = kw + 16 * rb + l16;
+    const int key = kp + 16 * rb + l16;
     if (key < Nk) {
       const int64_t o = (((int64_t)b * Nk + key) * Hkv + g) * D + 4 * grp;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const f32x4 a = acc_k[rb][db], e = acc_v[rb][db];
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(a[0] * scale, a[1] * scale);
-        wk[1] = pack_bf16x2(a[2] * scale, a[3] * scale);
-        wv[0] = pack_bf16x2(e[0], e[1]);
-        wv[1] = pack_bf16x2(e[2], e[3]);
-        *reinterpret_cast<u32x2*>(dk + o + 16 * db) = wk;
-        *reinterpret_cast<u32x2*>(dv + o + 16 * db) = wv;
+        const f32x4 a = acc[rb][db];
+        u32x2 u;
+        u[0] = pack_bf16x2(a[0] * f, a[1] * f);
+        u[1] = pack_bf16x2(a[2] * f, a[3] * f);
+        *reinterpret_cast<u32x2*>(dst + o + 16 * db) = u;
       }
     }
   }
@@ -583,23 +676,16 @@ __global__ __launch_bounds__(64 * WK, BWD_OCC) void bwd_dkdv_kernel(
 #ifndef BWD_RBQ
 #define BWD_RBQ 2
 #endif
-#ifndef BWD_WK
-#define BWD_WK 8
-#endif
-#ifndef BWD_RBK
-#define BWD_RBK 1
-#endif
 constexpr int kWQ = BWD_WQ, kRBQ = BWD_RBQ;    // bwd_dq: waves x 16-row blocks per wave
-constexpr int kWK = BWD_WK, kRBK = BWD_RBK;    // bwd_dkdv: waves x 16-key blocks per wave
 
 template <int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a) {
   const float c = a.scale * kLog2e;
+  const int ntq = (a.N + kT - 1) / kT;
   if ((int64_t)a.B * a.N * a.Hq > 0) {
-    const int64_t threads = (int64_t)a.B * a.N * a.Hq * (D / 8);
+    const int64_t threads = (int64_t)a.B * a.Hq * ntq * kT * (D / 8);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + kThr - 1) / kThr)), dim3(kThr), 0,
-                       a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.dsum, a.lse2, a.B, a.N,
-                       a.Hq);
+                       a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.ld, a.B, a.N, a.Hq, ntq);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -613,20 +699,19 @@ hipError_t launch(const BwdArgs& a) {
     if (grid > 0) {
       hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, kWQ, kRBQ>), dim3((unsigned)grid), dim3(64 * kWQ), 0, a.stream,
                          (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                         a.lse2, a.dsum, (uint16_t*)a.dq, a.N, a.Nk, a.Hq, a.Hkv, c, a.scale, n_qtiles, (int)n_work);
+                         a.ld, (uint16_t*)a.dq, a.N, a.Nk, a.Hq, a.Hkv, c, a.scale, ntq, n_qtiles, (int)n_work);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
   if (a.Nk > 0) {
-    constexpr int KEYS_G = 16 * kRBK * kWK;
-    const int n_ktiles = (a.Nk + KEYS_G - 1) / KEYS_G;
+    const int n_ktiles = (a.Nk + kDkKeys - 1) / kDkKeys;
     const int64_t n_work = (int64_t)a.B * a.Hkv * n_ktiles;
     const int64_t grid = (n_work + 7) / 8 * 8;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, kWK, kRBK>), dim3((unsigned)grid), dim3(64 * kWK), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse2, a.dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Nk, a.Hq,
-                       a.Hkv, c, a.scale, n_ktiles, (int)n_work);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(64 * kDkWaves), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                       a.ld, (uint16_t*)a.dk, (uint16_t*)a.dv, a.N, a.Nk, a.Hq, a.Hkv, c, a.scale, ntq, n_ktiles,
+                       (int)n_work);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

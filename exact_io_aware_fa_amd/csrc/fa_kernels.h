@@ -51,7 +51,8 @@ struct DecodeArgs {
 };
 
 // Backward (bf16): dq [B,N,Hq,d], dk/dv [B,Nk,Hkv,d] from q, k, v, o, dout and
-// the forward's lse [B,Hq,N]; dsum and lse2 are workspace arrays [B,Hq,N].
+// the forward's lse [B,Hq,N].  ld is the workspace [B*Hq][ceil(N/32)][64]
+// fp32: per 32-row query tile, the rows' base-2 LSE then their D.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -62,8 +63,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dsum;
-  float* lse2;
+  float* ld;
   int B, Hq, Hkv, N, Nk, d;
   bool causal;
   float scale;

@@ -453,22 +453,34 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
   // Every call issues the same copies: for an iteration past the last, the
   // views are empty, so the copies write zeros into a free stage and read
   // nothing; the waits below count copies.
-  auto issue = [&](const int it, const int st) __attribute__((always_inline)) {
-    const bool real = it < n_it;
-    const int ti = real ? ntq - 1 - it / G : 0;
-    const int h = g * G + (real ? it % G : 0);
-    const int i0 = ti * kT;
-    // view: row i0 of head h to the end of the slice (rows past N read 0)
-    const uint32_t bytes = real ? (uint32_t)((N - 1 - i0) * Hq + 1) * D * 2 : 0u;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + ((int64_t)i0 * Hq + h) * D, bytes);
+  // The iteration of the next copy (tile nx_ti of head g*G + nx_h), kept
+  // incrementally: the loop's scalar work is a large share of a step, and
+  // these need no division.  A view runs from row i0 of its head to row N-1
+  // (rows past N read 0), whatever the head.
+  int nx_it = 0, nx_h = 0;
+  const uint16_t* nx_row = src + ((int64_t)(ntq - 1) * kT * Hq + g * G) * D;   // row i0 of head g*G
+  uint32_t nx_bytes = (uint32_t)((N - 1 - (ntq - 1) * kT) * Hq + 1) * D * 2;
+  const float* nx_ld = ld + ((int64_t)(b * Hq + g * G) * ntq + ntq - 1) * (2 * kT);
+  auto issue = [&](const int st) __attribute__((always_inline)) {
+    const bool real = nx_it < n_it;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(nx_row + nx_h * D, real ? nx_bytes : 0u);
     char* dst = dma_t == 0 ? qS(st) : oS(st);
 #pragma unroll
     for (int i = 0; i < DMA_PW; ++i)
       buffer_load16_to_lds(r, voff[i], 0, (lds_void*)(dst + ((wave * DMA_PW + i) % INSTR_T) * 1024));
-    const __amdgpu_buffer_rsrc_t rl =
-        make_rsrc(ld + ((int64_t)(b * Hq + h) * ntq + ti) * (2 * kT), real ? 2 * kT * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(nx_ld, real ? 2 * kT * 4 : 0);
     if (lane < 2)
       buffer_load16_to_lds(rl, ld_voff, 0, (lds_void*)(reinterpret_cast<char*>(lS(st)) + LD_PW * wave));
+    if (real) {
+      ++nx_it;
+      nx_ld += (int64_t)ntq * (2 * kT);
+      if (++nx_h == G) {                        // next tile down, first head
+        nx_h = 0;
+        nx_row -= (int64_t)kT * Hq * D;
+        nx_bytes += (uint32_t)kT * Hq * D * 2;
+        nx_ld -= (int64_t)G * ntq * (2 * kT) + 2 * kT;
+      }
+    }
   };
 
   int r_off[2][DT];
@@ -542,11 +554,10 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
       wf[rb] = __builtin_bit_cast(bf16x8, u);
     }
   };
-  // wave A: P = 2^(s c - lse2) of iteration `it` (0 where masked; key
+  // wave A: P = 2^(s c - lse2) of the tile at row i0 (0 where masked; key
   // kp + 16rb + l16 is visible to query i0 + 8c + i iff key <= i0 + 8c + i +
   // offs), into wf and, in fp32, into the pair's slot of `pbuf`
-  auto soft_a = [&](const int it, const float* ldv, f32x4 (*pbuf)[RB][2][64]) __attribute__((always_inline)) {
-    const int i0 = (ntq - 1 - it / G) * kT;
+  auto soft_a = [&](const int i0, const float* ldv, f32x4 (*pbuf)[RB][2][64]) __attribute__((always_inline)) {
     const f32x4 la = *reinterpret_cast<const f32x4*>(&ldv[8 * grp]);
     const f32x4 lb = *reinterpret_cast<const f32x4*>(&ldv[8 * grp + 4]);
     const bool masked = CAUSAL && i0 + offs < kp + 16 * RB - 1;
@@ -594,11 +605,12 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
   // start of step t into the stage of tile t+PD-NS (last read in phase
   // 2t-1).
   constexpr int NS = kDkNS, PD = kDkNS - 2;
+  int cur_h = 0, cur_i0 = (ntq - 1) * kT;         // wave A: head index and first row of iteration t
   auto step = [&](const int t, const int ST) __attribute__((always_inline)) {
     const int SB = (ST + NS - 1) % NS;              // stage of tile t-1
     f32x4 (*p_cur)[RB][2][64] = (ST & 1) ? sP1 : sP0;
     f32x4 (*p_prev)[RB][2][64] = (ST & 1) ? sP0 : sP1;
-    issue(t + PD, (ST + PD) % NS);
+    issue((ST + PD) % NS);                  // iteration t + PD
     // (an MFMA phase issues all its LDS reads first: the transposed operands
     // of mm2, then the rows of mm1, which land while mm2 runs)
     if (role == 0) {
@@ -616,7 +628,11 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
       if (t >= 1) mm2();
       if (t < n_it) mm1();
     } else if (t < n_it) {
-      soft_a(t, lS(ST), p_cur);
+      soft_a(cur_i0, lS(ST), p_cur);
+      if (++cur_h == G) {                      // the tile of iteration t+1
+        cur_h = 0;
+        cur_i0 -= kT;
+      }
     }
     wait_vmem_le<(PD - 1) * (DMA_PW + 1)>();   // tile t+1 has landed
     barrier_no_fence();                        // ... for every wave
@@ -624,7 +640,7 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
 
   if (n_it > 0) {
 #pragma unroll
-    for (int t = 0; t < PD; ++t) issue(t, t);
+    for (int t = 0; t < PD; ++t) issue(t);
     wait_vmem_le<(PD - 1) * (DMA_PW + 1)>();
     barrier_no_fence();
     // steps 0..n_it, unrolled by NS so that every stage is named statically;

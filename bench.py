@@ -69,7 +69,7 @@ TRAFFIC_SOURCES = {
 # name also holds the prefill's fragment, so it comes later in this table).
 TRAFFIC_KERNELS = {
     "prefill": ("prefill_bf16_kernel", ["prefill_bf16_kernel"]),
-    "varlen_prefill": ("prefill_bf16_kernel<128, true, true>", ["prefill_bf16_kernel"]),
+    "varlen_prefill": ("prefill_bf16_kernel<128, true, true", ["prefill_bf16_kernel"]),
     "decode": ("decode_split_kernel<128, false>", ["decode_split_kernel", "decode_combine_kernel"]),
     "decode_paged": ("paged_prep_kernel", ["paged_prep_kernel", "decode_split_kernel", "decode_combine_kernel"]),
     "backward": ("bwd_pre_kernel", ["bwd_pre_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"]),
@@ -289,8 +289,10 @@ def prefill_bytes(cfg, elem_bytes):
 
 def device_info(torch):
     """The GPU's own figures, and the peaks derived from them: bf16 dense MFMA
-    = CUs x peak clock x 4096 flop/clk/CU; HBM = memory clock x 2 (double data
-    rate) x bus width / 8."""
+    = CUs x peak clock x 4096 flop/clk/CU; HBM = memory clock x 4 x bus width
+    / 8.  The factor 4: this part's HBM3E pins carry 8 Gb/s at the 2 GHz
+    memory clock the device reports (with 2 transfers per clock the 8192-bit
+    bus would peak at 4.1 TB/s, below what the decode alone measures)."""
     pr = torch.cuda.get_device_properties(0)
     cus, clk_khz = int(pr.multi_processor_count), int(getattr(pr, "clock_rate", 0))
     mem_khz, bus = int(getattr(pr, "memory_clock_rate", 0)), int(getattr(pr, "memory_bus_width", 0))
@@ -310,7 +312,7 @@ def device_info(torch):
     return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "cus": cus, "clock_mhz": clk_khz / 1000.0,
             "memory_clock_mhz": mem_khz / 1000.0, "memory_bus_width_bits": bus,
             "peak_bf16_tflops_derived": round(cus * clk_khz * 1e3 * 4096 / 1e12, 1),
-            "peak_hbm_gbs_derived": round(mem_khz * 1e3 * 2 * bus / 8 / 1e9, 1),
+            "peak_hbm_gbs_derived": round(mem_khz * 1e3 * 4 * bus / 8 / 1e9, 1),
             "peak_bf16_tflops_spec": MFMA_BF16_PEAK_TFLOPS, "peak_hbm_gbs_spec": HBM_PEAK_GBS}
 
 

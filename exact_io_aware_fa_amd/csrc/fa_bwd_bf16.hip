@@ -68,7 +68,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast
 
 // ---- The workspace ld [B*Hq][ntq][2*kT], ntq = ceil(N / kT): for query tile
 // t of (batch, head), lse2 of its rows (LSE log2(e); +inf for LSE = -inf and
-// for rows past N) then their D_i = dO_i . O_i (0 past N).  D/8 lanes per row.
+// for rows past N) then their D_i = dO_i . O_i (0 past N).  D/8 lanes per
+// row; the rows are taken in the BSHD order of O and dO (contiguous reads),
+// then the B*Hq*(ntq*kT - N) padding rows, one lane each.
 template <int D>
 __global__ __launch_bounds__(kThr) void bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                        const uint16_t* __restrict__ dout,
@@ -76,16 +78,12 @@ __global__ __launch_bounds__(kThr) void bwd_pre_kernel(const uint16_t* __restric
                                                        int N, int Hq, int ntq) {
   constexpr int LPR = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * kThr + threadIdx.x;
-  const int64_t prow = gid / LPR;                    // row of the padded [B*Hq][ntq*kT] range
+  const int64_t row = gid / LPR;
   const int part = (int)(gid % LPR);
-  const int64_t per_bh = (int64_t)ntq * kT;
-  const int64_t bh = prow / per_bh;
-  const int i = (int)(prow - bh * per_bh);
-  const bool valid = bh < (int64_t)B * Hq;
-  const bool in = valid && i < N;
+  const int64_t nrows = (int64_t)B * N * Hq;
+  const int pad = ntq * kT - N;
   float acc = 0.0f;
-  if (in) {
-    const int64_t row = ((bh / Hq) * N + i) * Hq + bh % Hq;
+  if (row < nrows) {
     const u32x4 a = load16(o + row * D + part * 8);
     const u32x4 g = load16(dout + row * D + part * 8);
 #pragma unroll
@@ -93,12 +91,27 @@ __global__ __launch_bounds__(kThr) void bwd_pre_kernel(const uint16_t* __restric
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (valid && part == 0) {
-    float* blk = ld + (bh * ntq + i / kT) * (2 * kT);
-    const float l = in ? lse[bh * N + i] : -INFINITY;
-    blk[i % kT] = l == -INFINITY ? INFINITY : l * kLog2e;
-    blk[kT + i % kT] = acc;
+  if (part != 0) return;
+  int64_t bh;
+  int i;
+  float l2;
+  if (row < nrows) {
+    const int h = (int)(row % Hq);
+    const int64_t bi = row / Hq;
+    i = (int)(bi % N);
+    bh = (bi / N) * Hq + h;
+    const float l = lse[bh * N + i];
+    l2 = l == -INFINITY ? INFINITY : l * kLog2e;
+  } else {
+    const int64_t r = row - nrows;               // padding row r of B*Hq*pad
+    if (pad == 0 || r >= (int64_t)B * Hq * pad) return;
+    bh = r / pad;
+    i = N + (int)(r % pad);
+    l2 = INFINITY;
   }
+  float* blk = ld + (bh * ntq + i / kT) * (2 * kT);
+  blk[i % kT] = l2;
+  blk[kT + i % kT] = acc;
 }
 
 // Copies of one 32-row tile of a [rows, H, D] tensor slice into LDS by THR
@@ -699,7 +712,7 @@ hipError_t launch(const BwdArgs& a) {
   const float c = a.scale * kLog2e;
   const int ntq = (a.N + kT - 1) / kT;
   if ((int64_t)a.B * a.N * a.Hq > 0) {
-    const int64_t threads = (int64_t)a.B * a.Hq * ntq * kT * (D / 8);
+    const int64_t threads = ((int64_t)a.B * a.N * a.Hq + (int64_t)a.B * a.Hq * (ntq * kT - a.N)) * (D / 8);
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((threads + kThr - 1) / kThr)), dim3(kThr), 0,
                        a.stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.ld, a.B, a.N, a.Hq, ntq);
     const hipError_t e = hipGetLastError();

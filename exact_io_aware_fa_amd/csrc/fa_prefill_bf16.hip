@@ -14,8 +14,10 @@
 // gfx950 mapping
 //  * workgroup = 8 waves = 384 query rows of one (batch, query head); wave w
 //    owns rows 48w..48w+47 as three 16-row blocks.  A KV tile is 32 keys.
-//    At head dim 64 (outside long causal launches) the workgroup is 256 rows,
-//    32 per wave, which fits two workgroups per CU.
+//    Smaller workgroups serve other launches (see the tile choice at the
+//    end): 256 rows (32 per wave, two workgroups per CU) for non-causal head
+//    dim 64, 128 rows (16 per wave) for causal head dim 64 up to 4096 rows
+//    and for head dim 128 launches with fewer 384-row tiles than CUs.
 //    Every K and V operand a wave reads from LDS feeds the MFMAs of its three
 //    row blocks, and a copied tile serves 384 rows.  On this chip a wave's
 //    MFMAs and another wave's softmax (exponentials above all) barely overlap
@@ -66,11 +68,13 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kBC = 32;             // keys per KV tile
 constexpr int kThreads = kWaves * 64;
-// Query rows per wave, RW: 48 (three 16-row blocks, one workgroup per CU) or,
-// at head dim 64, 32 (two blocks; at most 128 VGPRs, so two workgroups share a
-// CU and short sequences run in one round of resident workgroups).
+// Query rows per wave, RW: 48 (three 16-row blocks, one workgroup per CU),
+// 32 (two blocks, head dim 64 only: at most 128 VGPRs, so two workgroups share
+// a CU and short sequences run in one round of resident workgroups) or 16 (one
+// block: 128-row workgroups for launches with few query tiles; 59 VGPRs at
+// head dim 64, 104 at 128).
 template <int D, int RW>
-constexpr int waves_per_eu() { return RW == 32 ? 4 : 2; }
+constexpr int waves_per_eu() { return RW == 48 ? 2 : 4; }
 // Weights may exceed 1 by up to 2^kRescaleSlack before O is rescaled: fp32
 // sums and bf16 weights hold that exactly in range, and the rescale (vector
 // work on all accumulators) then happens only for an extreme jump of the max.
@@ -583,12 +587,23 @@ hipError_t launch(const PrefillArgs& a) {
 // slower with 32: its one round of resident workgroups pairs the long
 // diagonal-band tiles on shared CUs, where one workgroup per CU runs them in
 // LPT order.  (N is the longest query sequence for varlen.)
+//
+// 16 rows per wave (128-row workgroups, up to four per CU at head dim 64, two
+// at 128) shorten the longest workgroup's chain of key tiles, which bounds a
+// causal launch with few query tiles.  Against the sizes above, on one box:
+// causal B8 H12 N1024 d64 41.8 -> 37.2 us and B2 H16 N4096 d64 -12%, B1 H16
+// N8192 d64 +1% (kept at 48); non-causal B16 H16 N512 d64 +6% (kept at 32).
+// At head dim 128 they pay when the 384-row tiling leaves fewer tiles than
+// CUs: causal B2 H8 N1000 44.7 -> 23.4 us; B4 H16 N2048 (384 tiles) and B2
+// H32 N4096 (704) tie.
 template <bool VARLEN>
 hipError_t dispatch(const PrefillArgs& a) {
   if (a.d == 64) {
     if (!a.causal) return launch<64, false, VARLEN, 32>(a);
-    return a.N > 4096 ? launch<64, true, VARLEN, 48>(a) : launch<64, true, VARLEN, 32>(a);
+    return a.N > 4096 ? launch<64, true, VARLEN, 48>(a) : launch<64, true, VARLEN, 16>(a);
   }
+  if ((int64_t)a.B * a.Hq * ((a.N + 383) / 384) < 256)
+    return a.causal ? launch<128, true, VARLEN, 16>(a) : launch<128, false, VARLEN, 16>(a);
   return a.causal ? launch<128, true, VARLEN, 48>(a) : launch<128, false, VARLEN, 48>(a);
 }
 

@@ -39,10 +39,17 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
-    path = library_path()
+    _lib = open_library(library_path())
+    return _lib
+
+
+def open_library(path: str):
+    """Load one build of the library (its own copy of every kernel) and
+    declare its C signatures; the calls below use the one load_library()
+    returns.  Raises if the file is missing or its ABI version differs."""
     if not os.path.exists(path):
         raise RuntimeError(
-            "libfa.so is not built (%s); run __graft_entry__.build() or "
+            "%s is not built; run __graft_entry__.build() or "
             "python -m exact_io_aware_fa_amd.build" % path)
     lib = ctypes.CDLL(path)
     p, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -72,9 +79,8 @@ def load_library():
     lib.fa_abi_version.argtypes = []
     lib.fa_abi_version.restype = i32
     if lib.fa_abi_version() != ABI_VERSION:
-        raise RuntimeError("libfa.so ABI version %d, binding expects %d"
-                           % (lib.fa_abi_version(), ABI_VERSION))
-    _lib = lib
+        raise RuntimeError("%s: ABI version %d, binding expects %d"
+                           % (path, lib.fa_abi_version(), ABI_VERSION))
     return lib
 
 

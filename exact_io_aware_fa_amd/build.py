@@ -3,7 +3,9 @@
     python -m exact_io_aware_fa_amd.build
 
 Every source is compiled on every call (objects under _build/), then linked
-into exact_io_aware_fa_amd/libfa.so.  No GPU is needed: hipcc cross-compiles.
+into exact_io_aware_fa_amd/libfa.so; the same sources built with
+FA_DEBUG_SYNC give libfa_debug.so, which the race-check tests compare with
+it.  No GPU is needed: hipcc cross-compiles.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+DEBUG_LIB = os.path.join(PKG, "libfa_debug.so")   # FA_DEBUG_SYNC build: the race check's reference
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
@@ -69,6 +72,13 @@ def build(verbose: bool = False, out: str = LIB, defines: tuple = ()) -> str:
     return LIB_OUT
 
 
+def build_debug(verbose: bool = False) -> str:
+    """The same library with FA_DEBUG_SYNC: every copy and barrier drained in
+    order; its results must match libfa.so's bit for bit."""
+    return build(verbose=verbose, out=DEBUG_LIB, defines=("FA_DEBUG_SYNC=1",))
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_debug(verbose=True)
     sys.exit(0)

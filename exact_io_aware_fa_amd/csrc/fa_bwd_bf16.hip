@@ -314,6 +314,7 @@ __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
       for (int rb = 0; rb < RB; ++rb)
         acc[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dsf[rb], acc[rb][db], 0, 0, 0);
     }
+    if constexpr (kDebugSync) __syncthreads();
     if (more && copier) {
       // the other buffers were last read in iteration j-1, before its barrier
       ck.store(reinterpret_cast<char*>(sK[(j + 1) & 1]), tid);

@@ -6,6 +6,19 @@
 
 namespace fa {
 
+// FA_DEBUG_SYNC builds (the library's race check) run every pipeline in
+// order: each buffer->LDS copy is waited for as soon as it is issued, every
+// workgroup barrier first waits for all of the wave's memory operations, and
+// register-staged tiles get a barrier before they are stored.  The arithmetic
+// is the same instruction for instruction, so a debug build's results must
+// equal the fast build's bit for bit; a missing or short wait in the fast
+// pipelines would show as a difference.
+#ifdef FA_DEBUG_SYNC
+constexpr bool kDebugSync = true;
+#else
+constexpr bool kDebugSync = false;
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -112,6 +125,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
                                                      lds_void* lds_wave_base) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, soff, 0, 0);
+  if constexpr (kDebugSync) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 }
 
 // Wait until at most N of this wave's vector-memory operations (including
@@ -120,10 +134,11 @@ template <int N>
 __device__ __forceinline__ void wait_vmem_le() {
   // gfx9 s_waitcnt: vmcnt is bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]
   static_assert(N >= 0 && N < 64, "vmcnt field");
+  constexpr int M = kDebugSync ? 0 : N;
   // the fence keeps the scheduler from hoisting the wait above register-only
   // work that precedes it (it would then wait for the copies too early)
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+  __builtin_amdgcn_s_waitcnt(((M >> 4) << 14) | 0x0F70 | (M & 15));
 }
 __device__ __forceinline__ void wait_vmem_all() { wait_vmem_le<0>(); }
 
@@ -137,7 +152,7 @@ __device__ __forceinline__ void wait_vmem_all() { wait_vmem_le<0>(); }
 // barrier (without them register-only work is moved across it freely).
 __device__ __forceinline__ void barrier_no_fence() {
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt left open
+  __builtin_amdgcn_s_waitcnt(kDebugSync ? 0x0070 : 0xC07F);   // lgkmcnt(0); vmcnt, expcnt left open (debug: vmcnt(0))
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");

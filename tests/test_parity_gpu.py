@@ -167,12 +167,13 @@ def test_prefill_shapes(shape, causal, d, dtype):
 
 @pytest.mark.parametrize("N", [4096, 4100], ids=["N4096", "N4100"])
 def test_prefill_d64_causal_both_tile_heights(N):
-    """Head dim 64, causal: up to N = 4096 the launch uses 256-row workgroups
-    (32 rows per wave), above it 384-row ones (48 per wave); both sides of the
+    """Head dim 64, causal: up to N = 4096 the launch uses 128-row workgroups
+    (16 rows per wave), above it 384-row ones (48 per wave); both sides of the
     switch against the oracle, with ragged tails for both tile heights."""
     _say("case: prefill d64 causal N=%d" % N)
     q, k, v = inputs.prefill_inputs(1, N, N, 2, 1, 64, torch.bfloat16, seed=N)
     check_full(q, k, v, True, inputs.fp32_scale(64))
+
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_peaked_softmax_rows(dtype):

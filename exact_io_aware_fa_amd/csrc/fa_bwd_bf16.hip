@@ -44,6 +44,14 @@ constexpr int kThr = 256;       // threads of the staging copies and the pre ker
 
 __device__ __forceinline__ int pi16(int kb, int i) { return 8 * (i >> 2) + 4 * kb + (i & 3); }
 
+// Rows that exactly one workgroup reads (the dQ kernel's Q and dO rows, the
+// dK/dV kernel's K and V rows) are loaded non-temporal (policy bit NT):
+// streamed rather than allocated in L2, where they would evict the tiles
+// that the other workgroups of the head re-read.
+__device__ __forceinline__ u32x4 load16_once(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 2));
+}
+
 // XOR of the 16-byte chunk index by the row (bits b4..b0).  A tile is read
 // both ways: by rows (ds_read_b128 of one logical chunk of the 16 rows
 // pi16(kb, 0..15)) and transposed (ds_read_b64_tr_b16: chunks 2db, 2db+1 of
@@ -192,8 +200,8 @@ __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
     const uint32_t off = row >= 0 ? (uint32_t)row * q_row_bytes + grp * 16 : 0x80000000u;
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
-      qf[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(q_rsrc, off + t * 64));
-      df[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(d_rsrc, off + t * 64));
+      qf[rb][t] = __builtin_bit_cast(bf16x8, load16_once(q_rsrc, off + t * 64));
+      df[rb][t] = __builtin_bit_cast(bf16x8, load16_once(d_rsrc, off + t * 64));
     }
     const bool in = row >= 0 && row < N;
     const int ri = in ? row : 0;
@@ -441,7 +449,7 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
   for (int rb = 0; rb < RB; ++rb) {
     const uint32_t off = (uint32_t)(kp + 16 * rb + l16) * kv_row_bytes + grp * 16;
 #pragma unroll
-    for (int t = 0; t < DT; ++t) kvf[rb][t] = __builtin_bit_cast(bf16x8, buffer_load16(kv_rsrc, off + t * 64));
+    for (int t = 0; t < DT; ++t) kvf[rb][t] = __builtin_bit_cast(bf16x8, load16_once(kv_rsrc, off + t * 64));
   }
 
   // query tiles: causal row i sees key j iff j <= i + offs, so the

@@ -76,6 +76,7 @@ BWD_SHAPES = [
     (1, 2, 2, 530, 77),       # N > Nk: leading causal rows see no key
     (1, 4, 4, 1, 1),
     (1, 2, 1, 129, 300),      # tile tails on both sides
+    (1, 16, 1, 300, 333),     # a group of 16 heads walked innermost, ragged tiles
 ]
 
 

@@ -355,20 +355,17 @@ __global__ __launch_bounds__(64 * WQ, BWD_OCCQ) void bwd_dq_kernel(
 // keys, heads innermost: the workgroups of one kv head start on the same tile
 // and move through the tiles together, so they share each one in L2.
 // Per tile, wave A of a pair computes S = Q K^T, P (masked) and
-// dV^T += dO^T P, and leaves P (fp32) in LDS; wave B, one tile behind,
+// dV^T += dO^T P, and leaves P (fp32) in LDS; wave B, half a tile behind,
 // computes dP = dO V^T, dS = P o (dP - D) and dK^T += Q^T dS.  Both do the
-// same number of MFMAs per tile, and one's exponentials or dS arithmetic run
-// beside the other's products.  The tiles, with lse2 and D of their rows,
-// reach LDS by buffer_load ... lds through a ring of 4 stages, two tiles
-// ahead; one workgroup barrier per tile.
+// same number of MFMAs per tile; a tile has two phases (two workgroup
+// barriers), and in each one wave of every SIMD runs its MFMAs while the
+// other runs its exponentials or dS arithmetic.  The tiles, with lse2 and D
+// of their rows, reach LDS by buffer_load ... lds through a ring of 4
+// stages, two tiles ahead.
 constexpr int kDkWaves = 8;                         // 4 pairs
 constexpr int kDkRB = 2;                            // 16-key blocks per pair
 constexpr int kDkKeys = 16 * kDkRB * kDkWaves / 2;  // keys per workgroup
-#ifndef BWD_DK_NS
-#define BWD_DK_NS 4
-#endif
-constexpr int kDkNS = BWD_DK_NS;                    // stages of the Q/dO ring (copies run kDkNS - 2 tiles ahead)
-static_assert(kDkNS == 4 || kDkNS == 6, "ring of 4 or 6 stages (an even count keeps the P buffer static)");
+constexpr int kDkNS = 4;                            // stages of the Q/dO ring (copies run 2 tiles ahead)
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
@@ -393,31 +390,19 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(1024))) char sQ1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sQ2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sQ3[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sQ4[kDkNS > 4 ? TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char sQ5[kDkNS > 4 ? TILE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char sO0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sO1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sO2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sO3[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sO4[kDkNS > 4 ? TILE_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char sO5[kDkNS > 4 ? TILE_BYTES : 16];
   __shared__ __attribute__((aligned(256))) float sL0[2 * kT];   // lse2[kT], D[kT]
   __shared__ __attribute__((aligned(256))) float sL1[2 * kT];
   __shared__ __attribute__((aligned(256))) float sL2[2 * kT];
   __shared__ __attribute__((aligned(256))) float sL3[2 * kT];
-  __shared__ __attribute__((aligned(256))) float sL4[kDkNS > 4 ? 2 * kT : 4];
-  __shared__ __attribute__((aligned(256))) float sL5[kDkNS > 4 ? 2 * kT : 4];
   __shared__ __attribute__((aligned(1024))) f32x4 sP0[kDkWaves / 2][RB][2][64];   // P of a pair, by lane
   __shared__ __attribute__((aligned(1024))) f32x4 sP1[kDkWaves / 2][RB][2][64];
-  auto qS = [&](const int st) -> char* {
-    return st == 0 ? sQ0 : st == 1 ? sQ1 : st == 2 ? sQ2 : st == 3 ? sQ3 : st == 4 ? sQ4 : sQ5;
-  };
-  auto oS = [&](const int st) -> char* {
-    return st == 0 ? sO0 : st == 1 ? sO1 : st == 2 ? sO2 : st == 3 ? sO3 : st == 4 ? sO4 : sO5;
-  };
-  auto lS = [&](const int st) -> float* {
-    return st == 0 ? sL0 : st == 1 ? sL1 : st == 2 ? sL2 : st == 3 ? sL3 : st == 4 ? sL4 : sL5;
-  };
+  auto qS = [&](const int st) -> char* { return st == 0 ? sQ0 : st == 1 ? sQ1 : st == 2 ? sQ2 : sQ3; };
+  auto oS = [&](const int st) -> char* { return st == 0 ? sO0 : st == 1 ? sO1 : st == 2 ? sO2 : sO3; };
+  auto lS = [&](const int st) -> float* { return st == 0 ? sL0 : st == 1 ? sL1 : st == 2 ? sL2 : sL3; };
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   if (logical >= n_work) return;
@@ -676,12 +661,6 @@ __global__ __launch_bounds__(64 * kDkWaves, 1) void bwd_dkdv_kernel(
       if (s0 + 3 > n_it) return false;
       step(s0 + 3, 3);
       if (s0 + 4 > n_it) return false;
-      if constexpr (NS > 4) {
-        step(s0 + 4, 4);
-        if (s0 + 5 > n_it) return false;
-        step(s0 + 5, 5);
-        if (s0 + 6 > n_it) return false;
-      }
       return true;
     };
     for (int s0 = 0; round(s0); s0 += NS) {

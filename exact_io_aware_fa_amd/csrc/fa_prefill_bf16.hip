@@ -247,15 +247,44 @@ void prefill_bf16_kernel(
   // Tile j begins j*kBC rows into the slice.  Every call issues the same
   // number of copies: for a tile that does not exist (j >= n_kv) the view is
   // empty, so the copy writes zeros into a free stage and reads nothing; the
-  // waits below count copies.
-  auto issue = [&](const uint16_t* slice, const int j, const uint32_t* voff, char* stage) {
-    const bool real = j < n_kv;
-    const uint32_t tile_off = real ? (uint32_t)(j * kBC) * kv_row_bytes : 0u;
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(slice + (real ? (int64_t)j * kBC * Hkv * D : 0), real ? kv_bytes - tile_off : 0u);
+  // waits below count copies.  Each tensor's tiles are copied in order, so a
+  // cursor per tensor holds the next tile's index and, where kCursorCopy is
+  // set, its first row and the bytes left to the slice end: the descriptor
+  // then takes no multiplies and no branches, and the compiler can spread the
+  // few scalar instructions of a copy between the MFMAs it sits among.  With
+  // d = 128 and with 16-row waves that shortened the copying MFMA block by a
+  // measured 1-6%; with 32- and 48-row waves at d = 64 (the block is half as
+  // long there) it cost 1-3%, so those keep the address taken from the index.
+  constexpr bool kCursorCopy = D == 128 || RW == 16;
+  struct Cursor {
+    const uint16_t* base;   // the slice
+    const uint16_t* ptr;    // first row of tile j (kCursorCopy)
+    uint32_t left;          // bytes from ptr to the slice end (kCursorCopy)
+    int j;                  // next tile
+  };
+  Cursor kc{k_slice, k_slice, kv_bytes, 0}, vc{v_slice, v_slice, kv_bytes, 0};
+  auto issue = [&](Cursor& cur, const uint32_t* voff, char* stage) __attribute__((always_inline)) {
+    const bool real = cur.j < n_kv;
+    __amdgpu_buffer_rsrc_t r;
+    if constexpr (kCursorCopy) {
+      // (the cursor is wave-uniform; said explicitly, so that the descriptor
+      // stays in scalar registers)
+      const uint64_t pa = reinterpret_cast<uint64_t>(cur.ptr);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
+      const uint32_t bytes = __builtin_amdgcn_readfirstlane(real ? cur.left : 0u);
+      r = make_rsrc(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), bytes);
+      const uint32_t step = (uint32_t)kBC * kv_row_bytes;
+      cur.ptr += (int64_t)kBC * Hkv * D;
+      cur.left = cur.left > step ? cur.left - step : 0u;
+    } else {
+      const uint32_t tile_off = real ? (uint32_t)(cur.j * kBC) * kv_row_bytes : 0u;
+      r = make_rsrc(cur.base + (real ? (int64_t)cur.j * kBC * Hkv * D : 0), real ? kv_bytes - tile_off : 0u);
+    }
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i)
       buffer_load16_to_lds(r, voff[i], 0, (lds_void*)(stage + (dma_wave * DMA_PER_WAVE + i) * 1024));
+    ++cur.j;
   };
   constexpr int kCopiesPerBlock = 2 * DMA_PER_WAVE;
 
@@ -432,8 +461,8 @@ void prefill_bf16_kernel(
       __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);   // MFMAs of one K operand
     }
     if (decltype(copy_tag)::value) {
-      issue(k_slice, j + kPD, k_voff, kdst);
-      issue(v_slice, j + kPD - 1, v_voff, vdst);
+      issue(kc, k_voff, kdst);                      // K_{j+kPD}
+      issue(vc, v_voff, vdst);                      // V_{j+kPD-1}
     }
   };
   const auto kCopy = std::integral_constant<bool, true>();
@@ -509,9 +538,9 @@ void prefill_bf16_kernel(
       *reinterpret_cast<u32x2*>(vS(kNS - 1) + tid * 8) = u32x2{0u, 0u};
     if (group == 0) {
 #pragma unroll
-      for (int t = 0; t < kPD; ++t) issue(k_slice, t, k_voff, kS(t));
+      for (int t = 0; t < kPD; ++t) issue(kc, k_voff, kS(t));
 #pragma unroll
-      for (int t = 0; t < kPD - 1; ++t) issue(v_slice, t, v_voff, vS(t));
+      for (int t = 0; t < kPD - 1; ++t) issue(vc, v_voff, vS(t));
     }
     // both groups: the Q registers (and group 0's first copies) have landed.
     // (Waiting in one group only would leave the loads pending, as far as the
@@ -524,8 +553,8 @@ void prefill_bf16_kernel(
       // group 0's tail (stages named at run time: no LDS reads but one P.V)
       for (int j = n0; j < n_kv; ++j) {
         if (j == n0) stage_pv(vS((j + kNS - 1) % kNS));   // phase 2*n0: P.V of tile n0-1
-        issue(k_slice, j + kPD, k_voff, kS((j + kPD) % kNS));
-        issue(v_slice, j + kPD - 1, v_voff, vS((j + kPD - 1) % kNS));
+        issue(kc, k_voff, kS((j + kPD) % kNS));
+        issue(vc, v_voff, vS((j + kPD - 1) % kNS));
         barrier_no_fence();
         wait_vmem_le<(kPD - 1) * kCopiesPerBlock>();
         barrier_no_fence();

@@ -13,7 +13,9 @@ Prints one JSON line.  `value` is the prefill throughput in TFLOP/s counted as
 4*B*Hq*N*Nk*d/2 (the causal half), measured with HIP events around each
 launch on the launch stream; the decode part is reported beside it in GB/s of
 algorithmic bytes (K and V cache, q, o, lse and cu_seqlens, each once).
-After the timed steps, a chunked variable-length prefill (16 sequences of
+Every part below runs W times untimed before any part is timed (the chip's
+clocks settle only after some tens of ms of load).  After the timed steps, a
+chunked variable-length prefill (16 sequences of
 2048-token chunks on caches of 0..14336 earlier tokens, fa_fwd_varlen) is timed
 on its own and reported as `roofline_varlen_prefill`, counting 4*d*Hq flops
 per visible (query, key) pair.  Then the decode workload on a paged cache of
@@ -519,9 +521,24 @@ def main():
         print(json.dumps({"pmc_pass": True, "copy_bytes": PMC_COPY_BYTES}))
         return
 
+    # Every part resident, then every part's W untimed runs, then every part
+    # timed over K launches.  After idle the chip needs some tens of ms of load
+    # before its clocks settle (the first prefill launches of a fresh process
+    # run about 10% slower than later ones); warming all parts before timing
+    # any keeps the timed regions out of that ramp.  (The backward takes the
+    # forward's O and LSE, which the warm-up steps, or else the timed steps,
+    # have written before it first runs.)
+    varlen, vcfg, vq_lens, vk_lens = setup_varlen(torch, binding, inputs, dev)
+    vmax_k = int(vk_lens.max())
+    paged = setup_paged(torch, binding, inputs, dcfg, dev, max_len)
+    backward = setup_backward(torch, binding, pcfg, dev, qd, kd, vd, o, lse)
+    torch.cuda.synchronize()
     for _ in range(args.warmup):
         prefill()
         decode()
+    for part in (varlen, paged, backward):
+        for _ in range(args.warmup):
+            part()
     torch.cuda.synchronize()
 
     K = args.steps
@@ -548,57 +565,32 @@ def main():
     dbytes = decode_bytes(dcfg, total_len)
     gbs = dbytes / (dec_avg * 1e-3) / 1e9
 
-    # chunked variable-length prefill, timed on its own after the steps
-    varlen, vcfg, vq_lens, vk_lens = setup_varlen(torch, binding, inputs, dev)
-    vmax_k = int(vk_lens.max())
-    for _ in range(args.warmup):
-        varlen()
-    torch.cuda.synchronize()
-    va, vb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    va.record()
-    for _ in range(K):
-        varlen()
-    vb.record()
-    torch.cuda.synchronize()
-    var_ms = va.elapsed_time(vb) / K
+    def time_part(part):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(K):
+            part()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / K
+
+    # chunked variable-length prefill
+    var_ms = time_part(varlen)
     vflops = varlen_flops(vcfg, vq_lens, vk_lens)
     vtflops = vflops / (var_ms * 1e-3) / 1e12
 
-    # the decode workload on a paged cache, new rows appended, timed on its own
-    del varlen
-    paged = setup_paged(torch, binding, inputs, dcfg, dev, max_len)
-    for _ in range(args.warmup):
-        paged()
-    torch.cuda.synchronize()
-    pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    pa.record()
-    for _ in range(K):
-        paged()
-    pb.record()
-    torch.cuda.synchronize()
-    paged_ms = pa.elapsed_time(pb) / K
+    # the decode workload on a paged cache, new rows appended
+    paged_ms = time_part(paged)
     pbytes = paged_decode_bytes(dcfg, lens, PAGED_BLOCK)
     pgbs = pbytes / (paged_ms * 1e-3) / 1e9
 
-    # backward of the prefill workload, timed on its own
-    del paged
-    prefill()
-    backward = setup_backward(torch, binding, pcfg, dev, qd, kd, vd, o, lse)
-    for _ in range(args.warmup):
-        backward()
-    torch.cuda.synchronize()
-    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ga.record()
-    for _ in range(K):
-        backward()
-    gb.record()
-    torch.cuda.synchronize()
-    bwd_ms = ga.elapsed_time(gb) / K
+    # backward of the prefill workload
+    bwd_ms = time_part(backward)
     bflops = 2.5 * flops
     btflops = bflops / (bwd_ms * 1e-3) / 1e12
 
     # the three small prefill workloads, each on rotated input copies
-    del backward
+    del varlen, paged, backward
     small = {}
     for key, attr, copies in SMALL_PREFILL:
         scfg = getattr(inputs, attr)

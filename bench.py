@@ -353,7 +353,7 @@ def small_prefill_entry(cfg, ms, copies):
         return {"bound": "alu", "achieved": round(tflops, 4), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 5), "traffic": None, "ms": round(ms, 5),
                 "flops_per_launch": flops, "bytes_per_launch": nbytes,
-                "note": "one launch of one 256-row head: bound by launch and per-key latency, not by the ALU"}
+                "note": "one launch of one 256-row head: bound by the launch and a few memory round trips, not by the ALU"}
     nbytes = prefill_bytes(cfg, 2)
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

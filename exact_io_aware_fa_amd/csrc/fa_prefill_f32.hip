@@ -1,19 +1,29 @@
 // fa_prefill_f32.hip -- tiled exact attention forward in fp32 throughout, for
-// gfx950.  Same method as the bf16 kernel (K/V tiles streamed through LDS,
-// online softmax with a running row max and row sum, causal mask inside the
-// tile, fully masked tiles skipped; ai6s.net page, sections "FlashAttention
+// gfx950.  Same method as the bf16 kernel (K/V taken tile by tile, online
+// softmax with a running row max and row sum, causal mask inside the tile,
+// fully masked tiles skipped; ai6s.net page, sections "FlashAttention
 // changes the dataflow, not the algorithm" and "what ops-transformer adds"),
 // but every product and sum is an fp32 FMA on the vector ALU: no reduced-
 // precision matrix mode is involved, so the result stays within fp32 rounding
 // of exact attention.
 //
-// Mapping: a wave owns 64 / TPR query rows; TPR = D / 4 lanes share one row,
-// each holding 4 of its head-dim entries of q and of the output accumulator
-// (a row's dot products are summed across its lanes by a shuffle tree), so
-// that even one head of a few hundred rows spreads over many waves: the
-// single-head N = 256, d = 64 case takes 0.038 ms, against 0.153 ms with one
-// lane per row.
-// K and V tiles of 32 keys are staged in LDS and read as broadcasts.
+// Mapping: a workgroup owns ROWS = 64 / TPR query rows (TPR = D / 4 lanes
+// per row) and splits their key tiles over its kWaves waves: wave w takes
+// tiles w, w + kWaves, ..., with its own running max and sum, and the waves'
+// partial results are merged at the end (each partial is the softmax of its
+// own keys scaled by 2^(its max); the merge rescales them to the common max,
+// as the online softmax does between tiles).  Within a wave, a lane holds its
+// row's whole q and computes the full dot products of its KPL = 32 / TPR keys
+// of the tile, so a tile's row max takes one reduction over the row's lanes;
+// for the weighted sum of V a lane owns 4 head-dim entries of the row and
+// reads the tile's 32 weights of its row from a per-wave LDS buffer.  Keys
+// and rows past the end are read as 0 through bounded buffer views.  A lane's
+// loads go out in batches (a key's row, 8 or 16 keys' V slices), so that a
+// tile costs a few memory round trips rather than one per key.  Even one
+// head of a few hundred rows spreads over many waves with short chains of
+// dependent work: the single-head N = 256, d = 64 case (64 workgroups of 8
+// waves, one 32-key tile per wave) is bound by the launch and one tile's
+// latency.
 #include "fa_common.h"
 #include "fa_kernels.h"
 
@@ -21,19 +31,23 @@ namespace fa {
 namespace {
 
 constexpr int kTileKeys = 32;
-constexpr int kThreads = 64;
-constexpr int kSlice = 4;             // head-dim entries per lane
+constexpr int kWaves = 8;                 // waves per workgroup (key-tile split)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSlice = 4;                 // output head-dim entries per lane
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int N, int Nk, int Hq, int Hkv, float c,
     int n_qtiles, int n_work) {
   constexpr int TPR = D / kSlice;                 // lanes per query row
-  constexpr int ROWS = kThreads / TPR;            // query rows per workgroup
-  static_assert(TPR <= kThreads && ROWS * TPR == kThreads, "a row's lanes lie in one wave");
-  __shared__ __attribute__((aligned(16))) float sK[kTileKeys * D];
-  __shared__ __attribute__((aligned(16))) float sV[kTileKeys * D];
+  constexpr int ROWS = 64 / TPR;                  // query rows per workgroup
+  constexpr int KPL = kTileKeys / TPR;            // keys per lane in a tile's dot products
+  constexpr int DC = D / 4;                       // 16-byte chunks of a row
+  static_assert(ROWS * TPR == 64 && KPL * TPR == kTileKeys, "a row's lanes lie in one wave");
+  __shared__ __attribute__((aligned(16))) float sP[kWaves][ROWS][kTileKeys];   // a tile's weights by row
+  __shared__ float sM[kWaves][64], sL[kWaves][64];
+  __shared__ f32x4 sA[kWaves][64];
 
   const int logical = xcd_logical_block(blockIdx.x, gridDim.x);
   if (logical >= n_work) return;
@@ -50,24 +64,31 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
   const int q0 = qt * ROWS;
 
   const int tid = threadIdx.x;
-  const int row = q0 + tid / TPR;
-  const int part = tid % TPR;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int r = lane / TPR;                       // row of the lane within the workgroup
+  const int part = lane % TPR;
+  const int row = q0 + r;
   const int offs = Nk - N;
-  const int64_t q_row_stride = (int64_t)Hq * D;
-  const int64_t kv_row_stride = (int64_t)Hkv * D;
-  const float* kbase = k + ((int64_t)b * Nk * Hkv + g) * D;
-  const float* vbase = v + ((int64_t)b * Nk * Hkv + g) * D;
+  const uint32_t q_row_bytes = (uint32_t)Hq * D * 4;
+  const uint32_t kv_row_bytes = (uint32_t)Hkv * D * 4;
+  // bounded views of this (batch, head) q slice and (batch, kv head) K/V slices
+  const __amdgpu_buffer_rsrc_t q_rsrc = make_rsrc(q + ((int64_t)b * N * Hq + h) * D,
+                                                  (uint32_t)((N - 1) * Hq + 1) * D * 4);
+  const uint32_t kv_bytes = Nk > 0 ? (uint32_t)((Nk - 1) * Hkv + 1) * D * 4 : 0u;
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(k + ((int64_t)b * Nk * Hkv + g) * D, kv_bytes);
+  const __amdgpu_buffer_rsrc_t v_rsrc = make_rsrc(v + ((int64_t)b * Nk * Hkv + g) * D, kv_bytes);
+  auto ld4 = [](__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  };
 
-  float qv[kSlice], acc[kSlice];
-  {
-    const float* src = q + ((int64_t)b * N + row) * q_row_stride + (int64_t)h * D + part * kSlice;
+  f32x4 qf[DC];                                   // the row's q (0 past N)
 #pragma unroll
-    for (int e = 0; e < kSlice; ++e) {
-      qv[e] = row < N ? src[e] : 0.0f;
-      acc[e] = 0.0f;
-    }
-  }
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int t = 0; t < DC; ++t) qf[t] = ld4(q_rsrc, (uint32_t)row * q_row_bytes + t * 16);
+
+  float m_run = -INFINITY;                        // running max of the row (scaled, base 2)
+  float l_part = 0.0f;                            // this lane's share of the running row sum
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};               // head-dim entries 4*part.. of the row's output
 
   int n_kv = (Nk + kTileKeys - 1) / kTileKeys;
   if (CAUSAL) {
@@ -75,70 +96,99 @@ __global__ __launch_bounds__(kThreads) void prefill_f32_kernel(
     n_kv = last_key < 0 ? 0 : min(n_kv, last_key / kTileKeys + 1);
   }
 
-  for (int j = 0; j < n_kv; ++j) {
+  for (int j = wave; j < n_kv; j += kWaves) {
     const int j0 = j * kTileKeys;
-    __syncthreads();
-    for (int idx = tid; idx < kTileKeys * D / 4; idx += kThreads) {
-      const int r = idx / (D / 4), c4 = idx % (D / 4);
-      const int key = j0 + r;
-      f32x4 kw = {0.f, 0.f, 0.f, 0.f}, vw = {0.f, 0.f, 0.f, 0.f};
-      if (key < Nk) {
-        kw = *reinterpret_cast<const f32x4*>(kbase + (int64_t)key * kv_row_stride + c4 * 4);
-        vw = *reinterpret_cast<const f32x4*>(vbase + (int64_t)key * kv_row_stride + c4 * 4);
-      }
-      *reinterpret_cast<f32x4*>(&sK[r * D + c4 * 4]) = kw;
-      *reinterpret_cast<f32x4*>(&sV[r * D + c4 * 4]) = vw;
-    }
-    __syncthreads();
-
-    float s[kTileKeys];
+    float s[KPL];
     float mx = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < kTileKeys; ++jj) {
-      const float* kr = &sK[jj * D + part * kSlice];
-      float dot = 0.0f;
+    for (int i = 0; i < KPL; ++i) {
+      const int key = j0 + part * KPL + i;
+      // the key's row in batches of up to 16 loads (one memory round trip
+      // each; two at d = 128, where the row and q fill half the registers)
+      constexpr int KB = DC < 16 ? DC : 16;
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};         // four partial sums (independent chains)
 #pragma unroll
-      for (int e = 0; e < kSlice; ++e) dot = fmaf(qv[e], kr[e], dot);
+      for (int t0 = 0; t0 < DC; t0 += KB) {
+        f32x4 kr[KB];
 #pragma unroll
-      for (int off = 1; off < TPR; off <<= 1) dot += __shfl_xor(dot, off, 64);
-      const int key = j0 + jj;
+        for (int t = 0; t < KB; ++t) kr[t] = ld4(k_rsrc, (uint32_t)key * kv_row_bytes + (t0 + t) * 16);
+#pragma unroll
+        for (int t = 0; t < KB; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) d4[e] = fmaf(qf[t0 + t][e], kr[t][e], d4[e]);
+      }
+      const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
       const bool vis = key < Nk && (!CAUSAL || key <= row + offs);
-      s[jj] = vis ? dot * c : -INFINITY;
-      mx = fmaxf(mx, s[jj]);
+      s[i] = vis ? dot * c : -INFINITY;
+      mx = fmaxf(mx, s[i]);
     }
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
     const float m_new = fmaxf(m_run, mx);
     const float mu = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = fast_exp2(m_run - mu);        // 0 while nothing was visible
-    l_run *= alpha;
+    const float alpha = fast_exp2(m_run - mu);    // 0 while nothing was visible
+    l_part *= alpha;
+    acc *= alpha;
 #pragma unroll
-    for (int e = 0; e < kSlice; ++e) acc[e] *= alpha;
-#pragma unroll
-    for (int jj = 0; jj < kTileKeys; ++jj) {
-      const float p = fast_exp2(s[jj] - mu);
-      l_run += p;
-      const float* vr = &sV[jj * D + part * kSlice];
-#pragma unroll
-      for (int e = 0; e < kSlice; ++e) acc[e] = fmaf(p, vr[e], acc[e]);
+    for (int i = 0; i < KPL; ++i) {
+      const float p = fast_exp2(s[i] - mu);
+      l_part += p;
+      sP[wave][r][part * KPL + i] = p;
     }
+    // (the wave's LDS accesses run in order: the reads below see the writes
+    // above, and the next tile's writes follow these reads)
+    __builtin_amdgcn_wave_barrier();
+    // V in batches of VB keys (one round trip each)
+    constexpr int VB = D == 64 ? 16 : 8;
+#pragma unroll
+    for (int hb = 0; hb < kTileKeys / VB; ++hb) {
+      f32x4 vr[VB];
+#pragma unroll
+      for (int e = 0; e < VB; ++e) vr[e] = ld4(v_rsrc, (uint32_t)(j0 + VB * hb + e) * kv_row_bytes + part * 16);
+#pragma unroll
+      for (int k4 = 0; k4 < VB / 4; ++k4) {
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&sP[wave][r][VB * hb + 4 * k4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc += p4[e] * vr[4 * k4 + e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
     m_run = m_new;
+  }
+  // the row's sum over its lanes, then the merge of the waves' partials
+  float l_run = l_part;
+#pragma unroll
+  for (int off = 1; off < TPR; off <<= 1) l_run += __shfl_xor(l_run, off, 64);
+  sM[wave][lane] = m_run;
+  sL[wave][lane] = l_run;
+  sA[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  float m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sM[w][lane]);
+  const float mu = m == -INFINITY ? 0.0f : m;
+  float l = 0.0f;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float f = fast_exp2(sM[w][lane] - mu);  // 0 for a wave that saw no key
+    l = fmaf(sL[w][lane], f, l);
+    a += f * sA[w][lane];
   }
 
   if (row < N) {
-    const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-    float* dst = o + ((int64_t)b * N + row) * q_row_stride + (int64_t)h * D + part * kSlice;
-#pragma unroll
-    for (int e = 0; e < kSlice; e += 4) {
-      f32x4 w = {acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv};
-      *reinterpret_cast<f32x4*>(dst + e) = w;
-    }
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float* dst = o + ((int64_t)b * N + row) * ((int64_t)Hq * D) + (int64_t)h * D + part * kSlice;
+    *reinterpret_cast<f32x4*>(dst) = a * inv;
     if (part == 0)
-      lse[((int64_t)b * Hq + h) * N + row] = l_run > 0.0f ? (m_run + fast_log2(l_run)) * kLn2 : -INFINITY;
+      lse[((int64_t)b * Hq + h) * N + row] = l > 0.0f ? (m + fast_log2(l)) * kLn2 : -INFINITY;
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch(const PrefillArgs& a) {
-  constexpr int ROWS = kThreads / (D / kSlice);
+  constexpr int ROWS = 64 / (D / kSlice);
   const int n_qtiles = (a.N + ROWS - 1) / ROWS;
   const int64_t n_work = (int64_t)a.B * a.Hq * n_qtiles;
   if (n_work == 0) return hipSuccess;

@@ -633,9 +633,11 @@ def main():
                         "32 seqs L512-32768 (sum %d) Hq64 Hkv8 d128" % total_len,
             "prefill": {"B": pcfg.B, "Hq": pcfg.Hq, "Hkv": pcfg.Hkv, "N": pcfg.N, "Nk": pcfg.Nk,
                         "d": pcfg.d, "causal": pcfg.causal, "ms": round(pre_avg, 4),
+                        "ms_min": round(min(pre_ms), 4), "ms_max": round(max(pre_ms), 4),
                         "flops_per_launch": flops},
             "decode": {"B": dcfg.B, "Hq": dcfg.Hq, "Hkv": dcfg.Hkv, "d": dcfg.d,
                        "sum_len": total_len, "max_len": max_len, "ms": round(dec_avg, 4),
+                       "ms_min": round(min(dec_ms), 4), "ms_max": round(max(dec_ms), 4),
                        "bytes_per_launch": dbytes, "GB/s": round(gbs, 1),
                        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)},
             "varlen_prefill": {"B": vcfg.B, "Hq": vcfg.Hq, "Hkv": vcfg.Hkv, "d": vcfg.d, "causal": vcfg.causal,

@@ -439,7 +439,7 @@ void prefill_bf16_kernel(
   // distinct variables, so the compiler does not wait for the copies in
   // flight before the reads (the waits that order copies and reads are the
   // explicit ones below, before the workgroup barriers).
-  auto mblock = [&](const int j, const char* kread, const char* vread, char* kdst, char* vdst,
+  auto mblock = [&](const char* kread, const char* vread, char* kdst, char* vdst,
                     auto copy_tag) __attribute__((always_inline)) {
     // (tile 0's P.V reads the zero-filled stage of tile -1 with zero weights:
     // no branch, so both products share one scheduling region)
@@ -502,7 +502,7 @@ void prefill_bf16_kernel(
   auto run_group = [&](auto copy_tag, const int n_end) __attribute__((always_inline)) {
     constexpr bool COPY = decltype(copy_tag)::value;
     auto step = [&](const int j, const int st) __attribute__((always_inline)) {   // j % kNS == st
-      mblock(j, kS(st), vS((st + kNS - 1) % kNS), kS((st + kPD) % kNS), vS((st + kPD - 1) % kNS),
+      mblock(kS(st), vS((st + kNS - 1) % kNS), kS((st + kPD) % kNS), vS((st + kPD - 1) % kNS),
              copy_tag);                               // phase 2j+g
       barrier_no_fence();
       stage_softmax(j * kBC, j >= n_clean);           // phase 2j+1+g

@@ -175,6 +175,19 @@ def test_prefill_d64_causal_both_tile_heights(N):
     check_full(q, k, v, True, inputs.fp32_scale(64))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_prefill_f32_many_key_tiles_per_wave(causal, d):
+    """fp32 splits a workgroup's 32-key tiles over its 8 waves (wave w takes
+    tiles w, w+8, ...) and merges their partial softmaxes.  4100 keys (129
+    tiles, the last holding 4 keys) give each wave 16 or 17 tiles; 300
+    queries against them under the bottom-right causal mask see 3801 to 4100
+    keys each, so the mask cuts into the last tiles row by row."""
+    _say("case: prefill f32 N=300 Nk=4100 causal=%s d=%d" % (causal, d))
+    q, k, v = inputs.prefill_inputs(1, 300, 4100, 4, 2, d, torch.float32, seed=4400 + d)
+    check_full(q, k, v, causal, inputs.fp32_scale(d))
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 def test_peaked_softmax_rows(dtype):
     """Q scaled by 10: scores spread over about +-30, the running max moves

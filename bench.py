@@ -470,7 +470,7 @@ def main():
         mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU; this build has no multi-GPU path "
+        print("bench.py measures one GPU; the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 

@@ -1,5 +1,6 @@
 """Host-side logic of bench.py (CPU only): the algorithmic counts it divides
 by, and the attribution of counter dispatches to the parts of a launch."""
+import os
 import torch
 
 import bench
@@ -100,3 +101,15 @@ def test_small_prefill_copies_exceed_the_infinity_cache():
         cfg = getattr(inputs, attr)
         if cfg.dtype == torch.bfloat16:
             assert copies * bench.prefill_bytes(cfg, 2) > 256 * 2 ** 20, key
+
+
+def test_more_than_one_gpu_is_refused():
+    """The bench measures one GPU: --gpus other than 1 exits with status 2 and
+    a message before anything touches a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
